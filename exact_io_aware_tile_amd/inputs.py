@@ -1,0 +1,218 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle checks.
+
+This module draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the GPU library and the CPU oracle are fed from
+the same host bytes produced here.
+
+Recipe
+------
+* Every normal tensor is drawn as float32 N(0, 1) in C order of its logical
+  layout, in fixed chunks of ``CHUNK`` elements; chunk ``c`` of stream ``s``
+  under seed ``seed`` comes from ``numpy.random.default_rng([seed, s, c])``
+  (PCG64).  The values therefore do not depend on how many threads draw them.
+* Streams: q = 0, k = 1, v = 2 (the pages' q, k, v order).  Integer draws
+  (lengths, permutations, spike rows) use ``default_rng([seed, 100 + n])``.
+* bf16 tensors are the float32 draws rounded to nearest-even, kept as raw
+  ``uint16`` bit patterns; ``bf16_to_f32`` widens them back exactly.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+CHUNK = 1 << 22
+STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal_f32(seed: int, stream: int, shape) -> np.ndarray:
+    """float32 N(0,1) array of ``shape`` drawn chunk by chunk (see module doc)."""
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.float32)
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def fill(c: int) -> None:
+        lo = c * CHUNK
+        hi = min(n, lo + CHUNK)
+        rng = np.random.default_rng([seed, stream, c])
+        out[lo:hi] = rng.standard_normal(hi - lo, dtype=np.float32)
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest-even, returned as uint16 bit patterns.
+
+    Inputs here are finite normals, so no NaN/inf special-casing is needed.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+
+    def conv(lo: int, hi: int) -> None:
+        u = flat[lo:hi].view(np.uint32)
+        r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+        out[lo:hi] = (r >> np.uint32(16)).astype(np.uint16)
+
+    n = flat.size
+    if n <= CHUNK:
+        conv(0, n)
+    else:
+        spans = [(lo, min(n, lo + CHUNK)) for lo in range(0, n, CHUNK)]
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(lambda s: conv(*s), spans))
+    return out.reshape(x.shape)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32, exactly."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _maybe_bf16(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return f32_to_bf16(x)
+    raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+
+
+# --------------------------------------------------------------------------
+# dense batched attention: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d]
+# --------------------------------------------------------------------------
+def dense_case(seed: int, batch: int, nq: int, nk: int, hq: int, hkv: int, d: int,
+               dtype: str = "bf16", spike_frac: float = 0.0, spike_mult: float = 8.0) -> dict:
+    """Seeded dense case.  ``spike_frac`` > 0 multiplies round(spike_frac*nk)
+    key rows per (batch, head), chosen without replacement, by ``spike_mult``
+    (a power of two, so the scaling is exact after rounding)."""
+    q = normal_f32(seed, STREAM_Q, (batch, nq, hq, d))
+    k = normal_f32(seed, STREAM_K, (batch, nk, hkv, d))
+    v = normal_f32(seed, STREAM_V, (batch, nk, hkv, d))
+    spikes = None
+    if spike_frac > 0.0:
+        nsp = int(round(spike_frac * nk))
+        rng = np.random.default_rng([seed, 102])
+        spikes = np.empty((batch, hkv, nsp), dtype=np.int64)
+        for b in range(batch):
+            for h in range(hkv):
+                rows = np.sort(rng.choice(nk, size=nsp, replace=False))
+                spikes[b, h] = rows
+                k[b, rows, h, :] *= np.float32(spike_mult)
+    return {
+        "q": _maybe_bf16(q, dtype), "k": _maybe_bf16(k, dtype), "v": _maybe_bf16(v, dtype),
+        "dtype": dtype, "batch": batch, "nq": nq, "nk": nk, "hq": hq, "hkv": hkv, "d": d,
+        "spikes": spikes,
+    }
+
+
+# --------------------------------------------------------------------------
+# packed variable-length: q/k/v [T, H, d] with cu_seqlens [S+1]
+# --------------------------------------------------------------------------
+def varlen_lengths(seed: int, nseq: int, lo: int, hi: int) -> np.ndarray:
+    """nseq integer lengths, uniform on [lo, hi] inclusive."""
+    rng = np.random.default_rng([seed, 100])
+    return rng.integers(lo, hi, size=nseq, endpoint=True).astype(np.int64)
+
+
+def varlen_case(seed: int, lengths, hq: int, hkv: int, d: int, dtype: str = "bf16") -> dict:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    t = int(cu[-1])
+    q = normal_f32(seed, STREAM_Q, (t, hq, d))
+    k = normal_f32(seed, STREAM_K, (t, hkv, d))
+    v = normal_f32(seed, STREAM_V, (t, hkv, d))
+    return {
+        "q": _maybe_bf16(q, dtype), "k": _maybe_bf16(k, dtype), "v": _maybe_bf16(v, dtype),
+        "cu_seqlens": cu, "lengths": lengths, "total": t, "max_seqlen": int(lengths.max(initial=0)),
+        "dtype": dtype, "hq": hq, "hkv": hkv, "d": d,
+    }
+
+
+# --------------------------------------------------------------------------
+# paged decode: q [B, Hq, d]; pools [num_blocks, Hkv, block, d]; table [B, max_blocks]
+# --------------------------------------------------------------------------
+def paged_case(seed: int, seq_lens, hq: int, hkv: int, d: int, block_size: int = 16,
+               pad_blocks: int = 0) -> dict:
+    """One query token per sequence over a shuffled block pool (bf16).
+
+    num_blocks = sum(ceil(L/block)).  One seeded permutation of the pool
+    indices is dealt out in order: sequence b receives the next ceil(L_b/block)
+    entries.  Table slots past a sequence's last block hold -1.
+    ``pad_blocks`` extra unused slots are appended to every table row.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    nblk = (seq_lens + block_size - 1) // block_size
+    num_blocks = int(nblk.sum())
+    max_blocks = int(nblk.max(initial=0)) + int(pad_blocks)
+    perm = np.random.default_rng([seed, 101]).permutation(num_blocks).astype(np.int32)
+    table = np.full((len(seq_lens), max(1, max_blocks)), -1, dtype=np.int32)
+    pos = 0
+    for b, nb in enumerate(nblk):
+        table[b, :nb] = perm[pos:pos + nb]
+        pos += int(nb)
+    q = normal_f32(seed, STREAM_Q, (len(seq_lens), hq, d))
+    kp = normal_f32(seed, STREAM_K, (num_blocks, hkv, block_size, d))
+    vp = normal_f32(seed, STREAM_V, (num_blocks, hkv, block_size, d))
+    return {
+        "q": f32_to_bf16(q), "k_pool": f32_to_bf16(kp), "v_pool": f32_to_bf16(vp),
+        "block_table": table, "seq_lens": seq_lens.astype(np.int32), "num_blocks": num_blocks,
+        "block_size": block_size, "hq": hq, "hkv": hkv, "d": d, "dtype": "bf16",
+    }
+
+
+# --------------------------------------------------------------------------
+# the five named workloads
+# --------------------------------------------------------------------------
+def workload(n: int) -> dict:
+    """The five synthetic workloads (seed = workload number):
+
+    1. fp32 single head, batch 1, N = 256, d = 64, non-causal;
+    2. bf16 MHA causal prefill, batch 4, 32 heads, N = 2048, d = 128;
+    3. bf16 causal prefill, batch 1, 32 heads, N = 8192, d = 128, 1% of key
+       rows per head scaled by 8;
+    4. bf16 causal varlen prefill, 16 sequences of length U{128..4096},
+       32 heads, d = 64;
+    5. bf16 paged GQA decode, batch 64, 32 q heads / 8 kv heads, d = 128,
+       lengths U{1024..32768}, 16-token blocks.
+    """
+    if n == 1:
+        c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
+        c.update(causal=False, name="fp32 single-head N=256 d=64")
+        return c
+    if n == 2:
+        c = dense_case(2, 4, 2048, 2048, 32, 32, 128, dtype="bf16")
+        c.update(causal=True, name="bf16 causal MHA prefill B=4 H=32 N=2048 d=128")
+        return c
+    if n == 3:
+        c = dense_case(3, 1, 8192, 8192, 32, 32, 128, dtype="bf16", spike_frac=0.01)
+        c.update(causal=True, name="bf16 causal prefill B=1 H=32 N=8192 d=128, 1% key rows x8")
+        return c
+    if n == 4:
+        lens = varlen_lengths(4, 16, 128, 4096)
+        c = varlen_case(4, lens, 32, 32, 64, dtype="bf16")
+        c.update(causal=True, name="bf16 causal varlen prefill 16 seqs U{128..4096} H=32 d=64")
+        return c
+    if n == 5:
+        lens = varlen_lengths(5, 64, 1024, 32768)
+        c = paged_case(5, lens, 32, 8, 128, block_size=16)
+        c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    raise ValueError(f"no workload {n}")

@@ -1,0 +1,191 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's CPU-baseline leg
+may import this package.  The GPU library never imports it, and it never
+imports the GPU library: the two share no code.
+
+``oracle.c`` is the definition (materialised score row, textbook softmax,
+double precision); this module compiles it with gcc and wraps it with ctypes.
+``twin.py`` is an independent pure-Python brute force used to pin it, and
+``recurrence.py`` is the pages' tiled / paged / split recurrence in fp64,
+used to show that the method reaches the definition.
+
+Every function here is pinned by ``tests/test_oracle_*.py``; see the pin list
+in each test module's docstring.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F64, F32, BF16 = 0, 1, 2
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+           src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _load(path: str = _LIB):
+    global _lib
+    if _lib is not None and path == _LIB:
+        return _lib
+    if not os.path.exists(path) or (path == _LIB and os.path.getmtime(path) < os.path.getmtime(_SRC)):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_attn_dense.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, I, D, P, I64, P, P, I]
+    lib.oracle_attn_varlen.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P, I, D, P, I64, P, P, I]
+    lib.oracle_attn_decode_paged.argtypes = [P, P, P, I, P, P, P, I, P, I, I, I, I, I, I, D, P,
+                                             I64, P, P, I]
+    lib.oracle_max_threads.argtypes = [I]
+    for f in (lib.oracle_attn_dense, lib.oracle_attn_varlen, lib.oracle_attn_decode_paged,
+              lib.oracle_max_threads):
+        f.restype = I
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def load_library(path: str):
+    """Load an oracle build from an explicit path (used to test planted mistakes)."""
+    return _load(path)
+
+
+def threads(n: int = 0) -> int:
+    """Set (n > 0) and return the OpenMP thread count the oracle will use."""
+    return _load().oracle_max_threads(int(n))
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float64:
+        return F64
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"unsupported dtype {a.dtype}: use float64, float32 or uint16 (bf16 bits)")
+
+
+def _strides(a: np.ndarray, n: int) -> np.ndarray:
+    st = [s // a.itemsize for s in a.strides]
+    if st[-1] != 1:
+        raise ValueError("last dimension must be contiguous")
+    return np.asarray(st[:n], dtype=np.int64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.size)
+
+
+def dense(q, k, v, *, causal: bool, scale: float | None = None, rows=None, nthreads: int = 0,
+          lib=None):
+    """Dense batched attention.  q [B, Nq, Hq, d]; k, v [B, Nk, Hkv, d].
+
+    Returns (o, lse).  With rows=None: o [B, Hq, Nq, d] and lse [B, Hq, Nq];
+    otherwise rows are flattened ids (b*Hq + h)*Nq + i and o is [nrows, d].
+    Default scale is 1/sqrt(d) in double precision.
+    """
+    lib = lib or _load()
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r, nr = _rows(rows)
+    n = nr if r is not None else B * Hq * Nq
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    qs, ks, vs = _strides(q, 3), _strides(k, 3), _strides(v, 3)
+    st = lib.oracle_attn_dense(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Nq, Nk, Hq, Hkv, d,
+                               _ptr(qs), _ptr(ks), _ptr(vs), int(bool(causal)), scale, _ptr(r),
+                               nr, _ptr(o), _ptr(lse), int(nthreads))
+    if st:
+        raise ValueError(f"oracle_attn_dense failed with status {st}")
+    if r is None:
+        return o.reshape(B, Hq, Nq, d), lse.reshape(B, Hq, Nq)
+    return o, lse
+
+
+def varlen(q, k, v, cu_seqlens, *, causal: bool, scale: float | None = None, rows=None,
+           nthreads: int = 0, lib=None):
+    """Packed attention.  q [T, Hq, d]; k, v [T, Hkv, d]; cu_seqlens [S+1].
+
+    With rows=None: o [Hq, T, d], lse [Hq, T]; else rows are h*T + t.
+    """
+    lib = lib or _load()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r, nr = _rows(rows)
+    n = nr if r is not None else Hq * T
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    qs, ks, vs = _strides(q, 2), _strides(k, 2), _strides(v, 2)
+    st = lib.oracle_attn_varlen(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(cu), len(cu) - 1,
+                                Hq, Hkv, d, _ptr(qs), _ptr(ks), _ptr(vs), int(bool(causal)), scale,
+                                _ptr(r), nr, _ptr(o), _ptr(lse), int(nthreads))
+    if st:
+        raise ValueError(f"oracle_attn_varlen failed with status {st}")
+    if r is None:
+        return o.reshape(Hq, T, d), lse.reshape(Hq, T)
+    return o, lse
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, scale: float | None = None,
+                 rows=None, nthreads: int = 0, lib=None):
+    """Paged single-token decode.  q [B, Hq, d]; pools [num_blocks, Hkv, block, d]
+    (any strides with d contiguous; k and v pools must share strides);
+    block_table [B, max_blocks] int32; seq_lens [B] int32.
+
+    With rows=None: o [B, Hq, d], lse [B, Hq]; else rows are b*Hq + h.
+    """
+    lib = lib or _load()
+    B, Hq, d = q.shape
+    nb, Hkv, bs, _ = k_pool.shape
+    if k_pool.strides != v_pool.strides or k_pool.shape != v_pool.shape:
+        raise ValueError("k and v pools must have the same shape and strides")
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r, nr = _rows(rows)
+    n = nr if r is not None else B * Hq
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    qs, ps = _strides(q, 2), _strides(k_pool, 3)
+    st = lib.oracle_attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _dtype_code(q),
+                                      _ptr(qs), _ptr(ps), _ptr(bt), bt.shape[1], _ptr(sl), B, Hq,
+                                      Hkv, d, bs, nb, scale, _ptr(r), nr, _ptr(o), _ptr(lse),
+                                      int(nthreads))
+    if st:
+        raise ValueError(f"oracle_attn_decode_paged failed with status {st}")
+    if r is None:
+        return o.reshape(B, Hq, d), lse.reshape(B, Hq)
+    return o, lse
+
+
+def visible_pairs_dense(nq: int, nk: int, causal: bool) -> int:
+    """Number of visible (query, key) pairs of one head."""
+    if not causal:
+        return nq * nk
+    return sum(max(0, min(nk, i + (nk - nq) + 1)) for i in range(nq))

@@ -1,0 +1,293 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for exact attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * bench's CPU-baseline leg may load this library.  It shares no code with the
+ * GPU library and must never be used as a fallback for it.
+ *
+ * What it computes is the textbook definition that the tiled method reaches
+ * exactly up to float reassociation ("S12 FlashAttention",
+ * llminference.xinbetween.com, sections "Motivation / The problem" and the
+ * "What this unlocks beyond speed" tile "not an approximation"): for one query
+ * row i of one head,
+ *
+ *     s_j   = scale * sum_c q[i][c] * k[j][c]        for every visible key j
+ *     M     = max_j s_j
+ *     Z     = sum_j exp(s_j - M)
+ *     O[i]  = (sum_j exp(s_j - M) * v[j]) / Z
+ *     LSE_i = M + ln Z                                 (natural log)
+ *
+ * The whole score row s is materialised in a scratch array before the softmax
+ * (S is never tiled here).  Everything is double precision; inputs may be
+ * double, float or bf16 bit patterns and are widened exactly, element by
+ * element.  A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Visible keys:
+ *   - non-causal: every key;
+ *   - causal: key j is visible from query i iff j <= i + (Nk - Nq)  (queries
+ *     aligned to the end of the keys; identical to j <= i when Nq == Nk);
+ *   - packed variable length ("FlashAttention: The Algorithm That Beat the
+ *     Memory Wall", repo-explainer.com, section "Varlen Is the Quiet
+ *     Superpower"): only keys of the query's own sequence, causal in local
+ *     positions;
+ *   - paged decode ("S12 FlashAttention", section "Build it / Implementation",
+ *     the paged excerpt, and "How this composes with what you already built"):
+ *     logical key t of sequence b is pool[block_table[b][t / block]][g][t % block]
+ *     with g = h / (Hq / Hkv), for t < seq_len[b].
+ *
+ * Status codes: 0 ok, 1 bad argument, 2 out of memory.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+
+/* Widen element i of a typed buffer to double, exactly. */
+static double load(const void *p, int dtype, int64_t i) {
+  if (dtype == ORC_F64) return ((const double *)p)[i];
+  if (dtype == ORC_F32) return (double)((const float *)p)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/*
+ * One query row against an explicit list of key/value row offsets.
+ *   qoff        : element offset of the query row in q
+ *   koff[j]     : element offset of key row j in k, voff[j] likewise in v
+ *   n           : number of visible keys
+ *   s           : scratch of n doubles (the materialised score row)
+ *   o (d), lse  : outputs
+ */
+static void attend_row(const void *q, const void *k, const void *v, int dtype, int d,
+                       double scale, int64_t qoff, const int64_t *koff,
+                       const int64_t *voff, int64_t n, double *s, double *o,
+                       double *lse) {
+  for (int c = 0; c < d; ++c) o[c] = 0.0;
+  if (n <= 0) {
+    *lse = -INFINITY;
+    return;
+  }
+  /* S row: scaled dot products. */
+  for (int64_t j = 0; j < n; ++j) {
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += load(q, dtype, qoff + c) * load(k, dtype, koff[j] + c);
+    s[j] = scale * acc;
+  }
+  /* Row maximum. */
+  double m = s[0];
+  for (int64_t j = 1; j < n; ++j)
+    if (s[j] > m) m = s[j];
+  /* Unnormalised weights and their sum. */
+  double z = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    s[j] = exp(s[j] - m);
+    z += s[j];
+  }
+  /* Weighted sum of values, then normalise. */
+  for (int64_t j = 0; j < n; ++j)
+    for (int c = 0; c < d; ++c) o[c] += s[j] * load(v, dtype, voff[j] + c);
+  for (int c = 0; c < d; ++c) o[c] /= z;
+  *lse = m + log(z);
+}
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  return omp_get_max_threads();
+#else
+  (void)nthreads;
+  return 1;
+#endif
+}
+
+int oracle_max_threads(int nthreads) { return set_threads(nthreads); }
+
+/*
+ * Dense batched attention.  q is [B, Nq, Hq, d], k and v are [B, Nk, Hkv, d],
+ * addressed with element strides {batch, seq, head} (d is contiguous).
+ * Rows are flattened ids r = (b * Hq + h) * Nq + i; rows == NULL means all
+ * B*Hq*Nq rows in that order.  o is [nrows, d], lse is [nrows].
+ */
+int oracle_attn_dense(const void *q, const void *k, const void *v, int dtype, int B,
+                      int Nq, int Nk, int Hq, int Hkv, int d, const int64_t *qs,
+                      const int64_t *ks, const int64_t *vs, int causal, double scale,
+                      const int64_t *rows, int64_t nrows, double *o, double *lse,
+                      int nthreads) {
+  if (!q || !k || !v || !o || !lse || !qs || !ks || !vs) return 1;
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return 1;
+  if (!rows) nrows = (int64_t)B * Hq * Nq;
+  if (Nq == 0 && nrows > 0) return 1;
+  const int group = Hq / Hkv;
+  int bad = 0;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+    int64_t *koff = (int64_t *)malloc(sizeof(int64_t) * (size_t)(Nk > 0 ? Nk : 1));
+    int64_t *voff = (int64_t *)malloc(sizeof(int64_t) * (size_t)(Nk > 0 ? Nk : 1));
+    if (!s || !koff || !voff) {
+#pragma omp atomic write
+      bad = 2;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < nrows; ++r) {
+        int64_t id = rows ? rows[r] : r;
+        int64_t i = id % Nq, bh = id / Nq;
+        int64_t h = bh % Hq, b = bh / Hq;
+        if (id < 0 || b >= B) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        int64_t g = h / group;
+        int64_t last = causal ? i + (Nk - Nq) : (int64_t)Nk - 1; /* last visible key */
+        if (last > Nk - 1) last = Nk - 1;
+        int64_t n = last + 1 > 0 ? last + 1 : 0;
+        for (int64_t j = 0; j < n; ++j) {
+          koff[j] = b * ks[0] + j * ks[1] + g * ks[2];
+          voff[j] = b * vs[0] + j * vs[1] + g * vs[2];
+        }
+        attend_row(q, k, v, dtype, d, scale, b * qs[0] + i * qs[1] + h * qs[2], koff, voff,
+                   n, s, o + r * d, lse + r);
+      }
+    }
+    free(s);
+    free(koff);
+    free(voff);
+  }
+  return bad;
+}
+
+/*
+ * Packed variable-length attention.  q is [T, Hq, d], k and v [T, Hkv, d]
+ * with element strides {token, head}; sequence s owns tokens
+ * [cu[s], cu[s+1]).  Rows are flattened ids r = h * T + t (rows == NULL:
+ * all Hq*T).  Keys are the query's own sequence, causal in local positions.
+ */
+int oracle_attn_varlen(const void *q, const void *k, const void *v, int dtype,
+                       const int32_t *cu, int nseq, int Hq, int Hkv, int d,
+                       const int64_t *qs, const int64_t *ks, const int64_t *vs, int causal,
+                       double scale, const int64_t *rows, int64_t nrows, double *o,
+                       double *lse, int nthreads) {
+  if (!q || !k || !v || !cu || !o || !lse || !qs || !ks || !vs) return 1;
+  if (nseq < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return 1;
+  if (cu[0] != 0) return 1;
+  for (int s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return 1;
+  const int64_t T = cu[nseq];
+  int64_t maxlen = 1;
+  for (int s = 0; s < nseq; ++s)
+    if (cu[s + 1] - cu[s] > maxlen) maxlen = cu[s + 1] - cu[s];
+  if (!rows) nrows = (int64_t)Hq * T;
+  const int group = Hq / Hkv;
+  int bad = 0;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)maxlen);
+    int64_t *koff = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxlen);
+    int64_t *voff = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxlen);
+    if (!s || !koff || !voff) {
+#pragma omp atomic write
+      bad = 2;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < nrows; ++r) {
+        int64_t id = rows ? rows[r] : r;
+        int64_t t = id % (T > 0 ? T : 1), h = id / (T > 0 ? T : 1);
+        if (id < 0 || h >= Hq || T == 0) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        int seq = 0;
+        while (cu[seq + 1] <= t) ++seq; /* the sequence holding token t */
+        int64_t start = cu[seq], len = cu[seq + 1] - cu[seq];
+        int64_t i = t - start;
+        int64_t n = causal ? i + 1 : len;
+        int64_t g = h / group;
+        for (int64_t j = 0; j < n; ++j) {
+          koff[j] = (start + j) * ks[0] + g * ks[1];
+          voff[j] = (start + j) * vs[0] + g * vs[1];
+        }
+        attend_row(q, k, v, dtype, d, scale, t * qs[0] + h * qs[1], koff, voff, n, s,
+                   o + r * d, lse + r);
+      }
+    }
+    free(s);
+    free(koff);
+    free(voff);
+  }
+  return bad;
+}
+
+/*
+ * Paged decode: one query token per sequence.  q is [B, Hq, d] (element
+ * strides {batch, head}); the pools are addressed with element strides
+ * {block, head, token}; block_table is [B, max_blocks] (row stride
+ * max_blocks).  Rows are flattened ids r = b * Hq + h (rows == NULL: all).
+ * The query of sequence b sees its seq_lens[b] logical keys.
+ */
+int oracle_attn_decode_paged(const void *q, const void *kpool, const void *vpool, int dtype,
+                             const int64_t *qs, const int64_t *ps, const int32_t *block_table,
+                             int max_blocks, const int32_t *seq_lens, int B, int Hq, int Hkv,
+                             int d, int block_size, int num_blocks, double scale,
+                             const int64_t *rows, int64_t nrows, double *o, double *lse,
+                             int nthreads) {
+  if (!q || !kpool || !vpool || !qs || !ps || !block_table || !seq_lens || !o || !lse) return 1;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv || block_size <= 0) return 1;
+  int64_t maxlen = 1;
+  for (int b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_blocks * block_size) return 1;
+    if (seq_lens[b] > maxlen) maxlen = seq_lens[b];
+  }
+  if (!rows) nrows = (int64_t)B * Hq;
+  const int group = Hq / Hkv;
+  int bad = 0;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)maxlen);
+    int64_t *koff = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxlen);
+    if (!s || !koff) {
+#pragma omp atomic write
+      bad = 2;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < nrows; ++r) {
+        int64_t id = rows ? rows[r] : r;
+        int64_t h = id % Hq, b = id / Hq;
+        if (id < 0 || b >= B) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        int64_t g = h / group, n = seq_lens[b];
+        int oob = 0;
+        for (int64_t t = 0; t < n; ++t) {
+          int64_t phys = block_table[b * (int64_t)max_blocks + t / block_size];
+          if (phys < 0 || phys >= num_blocks) oob = 1;
+          koff[t] = phys * ps[0] + g * ps[1] + (t % block_size) * ps[2];
+        }
+        if (oob) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        /* the k and v pools share one addressing, so koff serves both */
+        attend_row(q, kpool, vpool, dtype, d, scale, b * qs[0] + h * qs[1], koff, koff, n, s,
+                   o + r * d, lse + r);
+      }
+    }
+    free(s);
+    free(koff);
+  }
+  return bad;
+}

@@ -1,0 +1,104 @@
+"""Planted mistakes in the oracle are caught by its pins (CPU only).
+
+Each case rewrites one spot of ``oracle/oracle.c`` into a plausible bug (a
+dropped term, a wrong sign, an off-by-one mask, a wrong group map, a wrong
+index), builds that copy with gcc into a temporary directory, swaps it in for
+the real oracle and runs the pin tests.  Every planted mistake must make at
+least one pin fail; the unmodified source must pass them all.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as P
+from tests import test_recurrence_cpu as R
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "scale dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "exp sign flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    "no normalisation": ("for (int c = 0; c < d; ++c) o[c] /= z;", "(void)z;"),
+    "lse without max": ("*lse = m + log(z);", "*lse = log(z);"),
+    "lse log2": ("*lse = m + log(z);", "*lse = m + log2(z);"),
+    "causal excludes diagonal": ("int64_t last = causal ? i + (Nk - Nq) :",
+                                 "int64_t last = causal ? i + (Nk - Nq) - 1 :"),
+    "causal top-left aligned": ("int64_t last = causal ? i + (Nk - Nq) :",
+                                "int64_t last = causal ? i :"),
+    "interleaved kv groups": ("        int64_t g = h / group;\n        int64_t last",
+                              "        int64_t g = h % Hkv;\n        int64_t last"),
+    "values reversed": ("o[c] += s[j] * load(v, dtype, voff[j] + c);",
+                        "o[c] += s[j] * load(v, dtype, voff[n - 1 - j] + c);"),
+    "key row reversed": ("load(k, dtype, koff[j] + c);", "load(k, dtype, koff[j] + (d - 1 - c));"),
+    "bf16 widening": ("uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;",
+                      "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 15;"),
+    "varlen causal off by one": ("int64_t n = causal ? i + 1 : len;", "int64_t n = causal ? i : len;"),
+    "paged slot index": ("(t % block_size) * ps[2];", "((t + 1) % block_size) * ps[2];"),
+    "paged group map": ("int64_t g = h / group, n = seq_lens[b];",
+                        "int64_t g = h % Hkv, n = seq_lens[b];"),
+    "max not subtracted in weights": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+}
+
+PINS = [
+    (P.test_worked_example_merge_rule, {}),
+    (P.test_rows_normalised, {"causal": True}),
+    (P.test_zero_query_is_mean, {"causal": True}),
+    (P.test_single_key, {}),
+    (P.test_causal_direction, {}),
+    (P.test_causal_prefix_property, {}),
+    (P.test_causal_end_aligned_when_more_keys, {}),
+    (P.test_gqa_group_mapping, {}),
+    (P.test_key_permutation_invariance, {}),
+    (P.test_score_shift, {}),
+    (P.test_brute_force_twin, {"shape": (2, 5, 7, 4, 2, 3), "causal": True}),
+    (P.test_torch_sdpa_fp64, {"shape": (2, 64, 64, 4, 2, 32), "causal": True}),
+    (P.test_varlen_equals_dense_per_sequence, {}),
+    (P.test_decode_equals_dense_over_gathered_keys, {}),
+    (P.test_bf16_widened_exactly, {}),
+    (R.test_tiled_causal_equals_oracle, {}),
+    (R.test_paged_equals_oracle, {"seq_len": 95}),
+]
+
+
+def _build(tmp_path, text, name):
+    src = tmp_path / f"{name}.c"
+    src.write_text(text)
+    out = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-shared", "-fPIC", str(src), "-o", str(out), "-lm"],
+                   check=True, capture_output=True)
+    return oracle.load_library(str(out))
+
+
+def _failures(monkeypatch, lib):
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = []
+    for fn, kw in PINS:
+        try:
+            fn(**kw)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(fn.__name__)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def source():
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    return open(SRC).read()
+
+
+def test_unmodified_oracle_passes_all_pins(tmp_path, monkeypatch, source):
+    lib = _build(tmp_path, source, "clean")
+    assert _failures(monkeypatch, lib) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, monkeypatch, source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) >= 1, f"mutation site for {name!r} not found in oracle.c"
+    lib = _build(tmp_path, source.replace(old, new), "m_" + name.replace(" ", "_"))
+    failed = _failures(monkeypatch, lib)
+    assert failed, f"planted mistake {name!r} passed every pin"
