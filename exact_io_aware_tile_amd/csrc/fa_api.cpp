@@ -1,0 +1,288 @@
+// fa_api.cpp -- the C ABI of include/fa.h: host-side validation, parameter
+// blocks and launch.  Nothing here touches device memory; every check runs
+// before any launch, and a rejected call launches nothing.
+//
+// The parameter block carries strides, data type, masking mode and sequence
+// layout to the kernels, the role "FlashAttention: The Algorithm That Beat
+// the Memory Wall" (repo-explainer.com, "How the Repo Connects Python to
+// Bare-Metal CUDA") gives the host glue.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa_status ok() {
+  g_last_error.clear();
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Vector loads move 16 bytes: every row start must be 16-byte aligned.
+bool strides_ok(const int64_t* s, int n, int64_t elems16) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || s[i] % elems16) return false;
+  return true;
+}
+
+float scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634073599); }
+
+constexpr int kDecodeBlock = 16;
+constexpr int kDecodeDim = 128;
+
+// Split size in tokens for the paged decode: explicit (num_splits > 0) or a
+// choice that gives every CU several workgroups without splitting finer
+// than needed.  Depends only on host-side sizes.
+int32_t decode_split_tokens(const fa_decode_paged_args* a) {
+  const int64_t maxlen = a->max_seq_len > 0 ? a->max_seq_len : 1;
+  int64_t splits;
+  if (a->num_splits > 0) {
+    splits = a->num_splits;
+  } else {
+    const int64_t pairs = (int64_t)a->batch * a->heads_kv;
+    const int64_t want = 4096;  // workgroups wanted in flight over 256 CUs
+    splits = pairs > 0 ? (want + pairs - 1) / pairs : 1;
+  }
+  int64_t st = (maxlen + splits - 1) / splits;
+  st = (st + kDecodeBlock - 1) / kDecodeBlock * kDecodeBlock;
+  if (a->num_splits <= 0) {
+    if (st > 1024) st = 1024;
+    if (st < 256) st = 256;
+  }
+  if (st < kDecodeBlock) st = kDecodeBlock;
+  return (int32_t)st;
+}
+
+int32_t decode_num_splits(const fa_decode_paged_args* a) {
+  const int64_t maxlen = a->max_seq_len > 0 ? a->max_seq_len : 1;
+  const int32_t st = decode_split_tokens(a);
+  return (int32_t)((maxlen + st - 1) / st);
+}
+
+fa_status check_decode(const fa_decode_paged_args* a) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: args is NULL");
+  if (a->batch < 0 || a->heads_q <= 0 || a->heads_kv <= 0 || a->max_seq_len < 0 ||
+      a->max_blocks_per_seq < 0 || a->num_blocks < 0 || a->num_splits < 0)
+    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: negative or zero size");
+  if (a->heads_q % a->heads_kv)
+    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: heads_q (%d) is not a multiple of heads_kv (%d)",
+                a->heads_q, a->heads_kv);
+  const int group = a->heads_q / a->heads_kv;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: heads_q / heads_kv = %d, supported 1, 2, 4, 8", group);
+  if (a->head_dim != kDecodeDim)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d, supported 128", a->head_dim);
+  if (a->block_size != kDecodeBlock)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: block_size %d, supported 16", a->block_size);
+  if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: max_seq_len %d exceeds max_blocks_per_seq * block_size",
+                a->max_seq_len);
+  if (a->batch > 65535) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: batch %d > 65535", a->batch);
+  return FA_OK;
+}
+
+size_t decode_workspace(const fa_decode_paged_args* a) {
+  const size_t rows = (size_t)a->batch * a->heads_q * (size_t)decode_num_splits(a);
+  return rows * (kDecodeDim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+FA_EXPORT fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd: args is NULL");
+  if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: negative or zero size");
+  if (a->heads_q % a->heads_kv)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
+                a->heads_kv);
+  if (a->dtype != FA_F32 && a->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: dtype %d", (int)a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head_dim %d, supported 64 and 128", a->head_dim);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: scale must be positive and finite");
+  if (a->batch == 0 || a->seqlen_q == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->o) return fail(FA_ERR_NULL_POINTER, "fa_fwd: q, k, v and o are required");
+  const int64_t e16 = a->dtype == FA_BF16 ? 8 : 4;
+  if (!strides_ok(a->q_stride, 3, e16) || !strides_ok(a->k_stride, 3, e16) || !strides_ok(a->v_stride, 3, e16) ||
+      !strides_ok(a->o_stride, 3, e16))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: strides must be non-negative multiples of %lld elements",
+                (long long)e16);
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: q, k, v, o must be 16-byte aligned");
+  const int64_t qtiles = (a->seqlen_q + fa::kFwdRowsPerTile - 1) / fa::kFwdRowsPerTile;
+  if (qtiles * a->heads_q * a->batch > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "fa_fwd: grid too large");
+
+  fa::FwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_seqlens = nullptr;
+  p.q_bs = a->q_stride[0], p.q_ss = a->q_stride[1], p.q_hs = a->q_stride[2];
+  p.k_bs = a->k_stride[0], p.k_ss = a->k_stride[1], p.k_hs = a->k_stride[2];
+  p.v_bs = a->v_stride[0], p.v_ss = a->v_stride[1], p.v_hs = a->v_stride[2];
+  p.o_bs = a->o_stride[0], p.o_ss = a->o_stride[1], p.o_hs = a->o_stride[2];
+  p.batch = a->batch;
+  p.seqlen_q = a->seqlen_q;
+  p.seqlen_k = a->seqlen_k;
+  p.total_tokens = 0;
+  p.heads_q = a->heads_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.num_qtiles = (int32_t)qtiles;
+  p.causal = a->causal ? 1 : 0;
+  p.scale_log2 = scale_log2(a->scale);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = a->dtype == FA_BF16 ? fa::launch_fwd_bf16(p, a->head_dim, s)
+                                           : fa::launch_fwd_f32(p, a->head_dim, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+FA_EXPORT fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen: args is NULL");
+  if (a->num_seqs < 0 || a->total_tokens < 0 || a->max_seqlen < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: negative or zero size");
+  if (a->heads_q % a->heads_kv)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
+                a->heads_kv);
+  if (a->dtype != FA_F32 && a->dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: dtype %d", (int)a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: head_dim %d, supported 64 and 128", a->head_dim);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: scale must be positive and finite");
+  if (a->num_seqs == 0 || a->max_seqlen == 0 || a->total_tokens == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->o || !a->cu_seqlens)
+    return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen: q, k, v, o and cu_seqlens are required");
+  const int64_t e16 = a->dtype == FA_BF16 ? 8 : 4;
+  if (!strides_ok(a->q_stride, 2, e16) || !strides_ok(a->k_stride, 2, e16) || !strides_ok(a->v_stride, 2, e16) ||
+      !strides_ok(a->o_stride, 2, e16))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: strides must be non-negative multiples of %lld elements",
+                (long long)e16);
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: q, k, v, o must be 16-byte aligned");
+  const int64_t qtiles = (a->max_seqlen + fa::kFwdRowsPerTile - 1) / fa::kFwdRowsPerTile;
+  if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: grid too large");
+
+  fa::FwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_seqlens = a->cu_seqlens;
+  p.q_bs = 0, p.q_ss = a->q_stride[0], p.q_hs = a->q_stride[1];
+  p.k_bs = 0, p.k_ss = a->k_stride[0], p.k_hs = a->k_stride[1];
+  p.v_bs = 0, p.v_ss = a->v_stride[0], p.v_hs = a->v_stride[1];
+  p.o_bs = 0, p.o_ss = a->o_stride[0], p.o_hs = a->o_stride[1];
+  p.batch = a->num_seqs;
+  p.seqlen_q = a->max_seqlen;
+  p.seqlen_k = a->max_seqlen;
+  p.total_tokens = a->total_tokens;
+  p.heads_q = a->heads_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.num_qtiles = (int32_t)qtiles;
+  p.causal = a->causal ? 1 : 0;
+  p.scale_log2 = scale_log2(a->scale);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = a->dtype == FA_BF16 ? fa::launch_fwd_bf16(p, a->head_dim, s)
+                                           : fa::launch_fwd_f32(p, a->head_dim, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_varlen: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) {
+  if (check_decode(a) != FA_OK) return 0;
+  return decode_workspace(a);
+}
+
+FA_EXPORT int32_t fa_decode_paged_num_splits(const fa_decode_paged_args* a) {
+  if (check_decode(a) != FA_OK) return 0;
+  return decode_num_splits(a);
+}
+
+FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream) {
+  const fa_status st = check_decode(a);
+  if (st != FA_OK) return st;
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: scale must be positive and finite");
+  if (a->batch == 0) return ok();
+  if (!a->q || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens || !a->o || !a->workspace)
+    return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: q, pools, block_table, seq_lens, o, workspace required");
+  if (!strides_ok(a->pool_stride, 3, 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
+    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: strides must be non-negative multiples of 8 elements");
+  if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->o) ||
+      !aligned16(a->workspace))
+    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: q, pools, o and workspace must be 16-byte aligned");
+  const size_t need = decode_workspace(a);
+  if (a->workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode_paged: workspace %zu bytes, need %zu", a->workspace_bytes,
+                need);
+
+  fa::DecodeParams p{};
+  p.q = a->q;
+  p.k_pool = a->k_pool;
+  p.v_pool = a->v_pool;
+  p.p_bs = a->pool_stride[0], p.p_hs = a->pool_stride[1], p.p_ts = a->pool_stride[2];
+  p.q_bs = a->q_stride[0], p.q_hs = a->q_stride[1];
+  p.o_bs = a->o_stride[0], p.o_hs = a->o_stride[1];
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.num_splits = decode_num_splits(a);
+  p.split_tokens = decode_split_tokens(a);
+  const size_t rows = (size_t)a->batch * a->heads_q * (size_t)p.num_splits;
+  p.ws_o = (float*)a->workspace;
+  p.ws_ml = p.ws_o + rows * kDecodeDim;
+  p.batch = a->batch;
+  p.heads_q = a->heads_q;
+  p.heads_kv = a->heads_kv;
+  p.group = a->heads_q / a->heads_kv;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.max_seq_len = a->max_seq_len;
+  p.scale_log2 = scale_log2(a->scale);
+  const hipError_t e = fa::launch_decode_paged(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode_paged: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+FA_EXPORT const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_POINTER: return "null pointer";
+    case FA_ERR_BAD_SHAPE: return "bad shape or layout";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+FA_EXPORT const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+FA_EXPORT int32_t fa_abi_version(void) { return FA_ABI_VERSION; }

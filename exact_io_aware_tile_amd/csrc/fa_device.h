@@ -1,0 +1,53 @@
+// fa_device.h -- gfx950 device helpers: MFMA wrappers, bf16 packing,
+// base-2 transcendental wrappers and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr float kLn2 = 0.693147180559945309417f;
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).
+// Lane l supplies A[l % 32][8 * (l / 32) + j] and B[8 * (l / 32) + j][l % 32]
+// for j = 0..7; accumulator register r of lane l holds
+// D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32 fp32) += A(32x2 fp32) * B(2x32 fp32); lane l supplies
+// A[l % 32][l / 32] and B[l / 32][l % 32]; same accumulator layout.
+__device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 halves of a 32-bit word, widened exactly.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word, lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Value held by lane (l ^ 32) -- the other half of a 64-wide wave.
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+}  // namespace fa

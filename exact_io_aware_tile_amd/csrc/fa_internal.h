@@ -1,0 +1,61 @@
+// fa_internal.h -- parameter blocks and launchers shared by the host API and
+// the kernel translation units of libfa_gfx950.so.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Query rows handled by one prefill workgroup (both dtypes).
+constexpr int kFwdRowsPerTile = 128;
+
+// One prefill launch: dense batched attention or packed variable-length
+// sequences.  All strides are in elements.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                 // may be null
+  const int32_t* cu_seqlens;  // null: dense; else packed sequences
+  int64_t q_bs, q_ss, q_hs;   // batch (dense only), token, head strides
+  int64_t k_bs, k_ss, k_hs;
+  int64_t v_bs, v_ss, v_hs;
+  int64_t o_bs, o_ss, o_hs;
+  int32_t batch;     // dense batch, or number of packed sequences
+  int32_t seqlen_q;  // dense lengths; for packed sequences: max_seqlen bound
+  int32_t seqlen_k;
+  int32_t total_tokens;  // packed only: LSE row stride
+  int32_t heads_q;
+  int32_t group;         // heads_q / heads_kv
+  int32_t num_qtiles;    // query tiles per (sequence, head)
+  int32_t causal;
+  float scale_log2;      // scale * log2(e): scores are kept in base 2
+};
+
+// Paged decode: split kernel followed by the combine kernel.
+struct DecodeParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  int64_t p_bs, p_hs, p_ts;  // pool strides: block, head, token
+  int64_t q_bs, q_hs;
+  int64_t o_bs, o_hs;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  float* ws_o;   // [batch, heads_q, num_splits, head_dim] fp32 partial o
+  float* ws_ml;  // [batch, heads_q, num_splits, 2] fp32 partial (m, l), m in base 2
+  int32_t batch, heads_q, heads_kv, group, max_blocks, max_seq_len;
+  int32_t num_splits;       // grid extent in splits
+  int32_t split_tokens;     // tokens per split, a multiple of the block size
+  float scale_log2;
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,243 @@
+"""Thin ctypes binding over libfa_gfx950.so (declared in include/fa.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the attention runs in the library's kernels.  There is
+no fallback -- if the library is missing or a call is rejected, an exception
+is raised.
+
+Layouts (see include/fa.h):
+    fa_fwd:          q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o like q, lse [B, Hq, Nq]
+    fa_fwd_varlen:   q [T, Hq, d], k/v [T, Hkv, d], cu_seqlens int32 [S+1] -> o, lse [Hq, T]
+    fa_decode_paged: q [B, Hq, d], pools [blocks, Hkv, 16, d] (or any strides with d
+                     contiguous), block_table int32 [B, max_blocks], seq_lens int32 [B]
+                     -> o [B, Hq, d], lse [B, Hq]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_gfx950.so")
+
+FA_OK, FA_ERR_NULL_POINTER, FA_ERR_BAD_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_HIP = range(6)
+FA_F32, FA_BF16 = 0, 1
+
+_P, _I32, _I64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o", _P), ("lse", _P),
+                ("batch", _I32), ("seqlen_q", _I32), ("seqlen_k", _I32), ("heads_q", _I32),
+                ("heads_kv", _I32), ("head_dim", _I32),
+                ("q_stride", _I64 * 3), ("k_stride", _I64 * 3), ("v_stride", _I64 * 3),
+                ("o_stride", _I64 * 3),
+                ("dtype", ctypes.c_int), ("scale", _F), ("causal", _I32)]
+
+
+class FwdVarlenArgs(ctypes.Structure):
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o", _P), ("lse", _P), ("cu_seqlens", _P),
+                ("num_seqs", _I32), ("total_tokens", _I32), ("max_seqlen", _I32), ("heads_q", _I32),
+                ("heads_kv", _I32), ("head_dim", _I32),
+                ("q_stride", _I64 * 2), ("k_stride", _I64 * 2), ("v_stride", _I64 * 2),
+                ("o_stride", _I64 * 2),
+                ("dtype", ctypes.c_int), ("scale", _F), ("causal", _I32)]
+
+
+class DecodePagedArgs(ctypes.Structure):
+    _fields_ = [("q", _P), ("k_pool", _P), ("v_pool", _P), ("pool_stride", _I64 * 3),
+                ("block_table", _P), ("seq_lens", _P), ("o", _P), ("lse", _P),
+                ("q_stride", _I64 * 2), ("o_stride", _I64 * 2),
+                ("batch", _I32), ("heads_q", _I32), ("heads_kv", _I32), ("head_dim", _I32),
+                ("block_size", _I32), ("max_blocks_per_seq", _I32), ("num_blocks", _I32),
+                ("max_seq_len", _I32), ("scale", _F), ("num_splits", _I32),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_paged", "fa_decode_paged_workspace_size",
+           "fa_decode_paged_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+def lib(path: str = LIB_PATH):
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m exact_io_aware_tile_amd.build`")
+    L = ctypes.CDLL(path)
+    L.fa_fwd.argtypes = [ctypes.POINTER(FwdArgs), _P]
+    L.fa_fwd.restype = ctypes.c_int
+    L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), _P]
+    L.fa_fwd_varlen.restype = ctypes.c_int
+    L.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
+    L.fa_decode_paged.restype = ctypes.c_int
+    L.fa_decode_paged_workspace_size.argtypes = [ctypes.POINTER(DecodePagedArgs)]
+    L.fa_decode_paged_workspace_size.restype = ctypes.c_size_t
+    L.fa_decode_paged_num_splits.argtypes = [ctypes.POINTER(DecodePagedArgs)]
+    L.fa_decode_paged_num_splits.restype = _I32
+    L.fa_status_string.argtypes = [ctypes.c_int]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_abi_version.argtypes = []
+    L.fa_abi_version.restype = _I32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        L = lib()
+        raise FAError(status, f"{L.fa_status_string(status).decode()}: {L.fa_last_error().decode()}")
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling helpers (torch is only memory + streams here)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.float32 or torch.bfloat16")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+    for t in ts:
+        if t is not None and t.dim() > 0 and t.stride(-1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def fa_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
+           return_lse: bool = True, stream=None):
+    """Dense attention.  Returns (o, lse) (lse is None when return_lse is False)."""
+    torch = _torch()
+    _dev(q, k, v, out, lse)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    a = FwdArgs()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = B, Nq, Nk, Hq, Hkv, d
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, name)[:] = list(t.stride()[:3])
+    a.dtype = _dtype_code(q)
+    a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a.causal = int(bool(causal))
+    _check(lib().fa_fwd(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = True,
+                  scale: float | None = None, out=None, lse=None, return_lse: bool = True,
+                  stream=None):
+    """Packed variable-length attention.  ``max_seqlen`` is a host-side bound."""
+    torch = _torch()
+    _dev(q, k, v, out, lse, cu_seqlens)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    a = FwdVarlenArgs()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.num_seqs, a.total_tokens, a.max_seqlen = cu_seqlens.numel() - 1, T, int(max_seqlen)
+    a.heads_q, a.heads_kv, a.head_dim = Hq, Hkv, d
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, name)[:] = list(t.stride()[:2])
+    a.dtype = _dtype_code(q)
+    a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a.causal = int(bool(causal))
+    _check(lib().fa_fwd_varlen(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, num_splits):
+    B, Hq, d = q.shape
+    nb, Hkv, bs, _ = k_pool.shape
+    if tuple(k_pool.stride()) != tuple(v_pool.stride()) or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must share shape and strides")
+    a = DecodePagedArgs()
+    a.q, a.k_pool, a.v_pool = _ptr(q), _ptr(k_pool), _ptr(v_pool)
+    ps = k_pool.stride()
+    a.pool_stride[:] = [ps[0], ps[1], ps[2]]
+    a.block_table, a.seq_lens = _ptr(block_table), _ptr(seq_lens)
+    a.q_stride[:] = list(q.stride()[:2])
+    a.batch, a.heads_q, a.heads_kv, a.head_dim, a.block_size = B, Hq, Hkv, d, bs
+    a.max_blocks_per_seq = block_table.shape[1] if block_table is not None else 0
+    a.num_blocks, a.max_seq_len = nb, int(max_seq_len)
+    a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a.num_splits = int(num_splits)
+    return a
+
+
+def fa_decode_paged_workspace_size(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, *,
+                                   num_splits: int = 0) -> int:
+    a = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, None, num_splits)
+    return int(lib().fa_decode_paged_workspace_size(ctypes.byref(a)))
+
+
+def fa_decode_paged_num_splits(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, *,
+                               num_splits: int = 0) -> int:
+    a = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, None, num_splits)
+    return int(lib().fa_decode_paged_num_splits(ctypes.byref(a)))
+
+
+def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, *,
+                    scale: float | None = None, num_splits: int = 0, out=None, lse=None,
+                    return_lse: bool = True, workspace=None, stream=None):
+    """Paged single-token decode.  Returns (o, lse)."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    a = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, num_splits)
+    a.o, a.lse = _ptr(out), _ptr(lse)
+    a.o_stride[:] = list(out.stride()[:2])
+    need = int(lib().fa_decode_paged_workspace_size(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(lib().fa_decode_paged(ctypes.byref(a), _stream(stream)))
+    return out, lse

@@ -1,0 +1,196 @@
+/*
+ * fa.h -- C ABI of libfa_gfx950.so: exact attention on MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention as a stream over
+ * key/value tiles with the online-softmax recurrence -- a running row max m,
+ * a running sum l, the correction alpha = exp(m_old - m_new) applied to the
+ * output accumulator o, and a final o / l -- so the N x N score matrix never
+ * reaches device memory.  Sources (page titles and sections):
+ *   - "S12 FlashAttention" (llminference.xinbetween.com): "Core idea / The
+ *     solution" (the recurrence), "Mechanics / How it works" (tiles in fast
+ *     on-chip memory), "What this unlocks beyond speed" (paged tiles,
+ *     flash-decoding split and combine), "How this composes with what you
+ *     already built" (block table + GQA in one decode loop), "Build it /
+ *     Implementation" (paged excerpt; the fully masked tile NaN guard);
+ *   - "FlashAttention" (tachyon.techntrek.in/learn/flash-attention), "For
+ *     engineers / Show the maths": the (m, l) merge rule;
+ *   - "FlashAttention: The Algorithm That Beat the Memory Wall"
+ *     (repo-explainer.com/hillfate/flash-attention): "A Tile, a Register
+ *     File, and a Trick Called Online Softmax" (outer loop over query tiles,
+ *     inner loop over key/value tiles), "How the Repo Connects Python to
+ *     Bare-Metal CUDA" (strides, dtypes, masking mode and sequence layout
+ *     carried in a parameter struct), "Varlen Is the Quiet Superpower"
+ *     (packed sequences, no padding).
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or retains them, and keeps no state
+ *     between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream and returns; nothing
+ *     synchronises.  Faults during execution surface at the caller's next
+ *     synchronisation.
+ *   - Strides are in ELEMENTS; the head dimension d must be contiguous.
+ *   - Scores are s = scale * q . k with `scale` given by the caller (1/sqrt(d)
+ *     is the usual choice).  LSE is the natural log of the sum over visible
+ *     keys of exp(s), in fp32.  A query with no visible key gets O = 0 and
+ *     LSE = -inf.
+ *   - Causal masking is aligned to the END of the keys: key j is visible
+ *     from query i iff j <= i + (Nk - Nq)  (plain j <= i when Nq == Nk).
+ *   - GQA: heads_q must be a multiple of heads_kv; query head h reads key /
+ *     value head h / (heads_q / heads_kv).
+ *   - Validation runs on the host before any launch.  On any error nothing
+ *     is launched, no output is written, and fa_last_error() describes it.
+ *     No C++ exception crosses this interface.  Calls are re-entrant on
+ *     distinct streams.
+ */
+#ifndef FA_GFX950_H
+#define FA_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,          /* negative size, heads_q % heads_kv != 0, bad stride ... */
+  FA_ERR_UNSUPPORTED = 3,        /* valid but not built: dtype / head_dim / block_size */
+  FA_ERR_WORKSPACE_TOO_SMALL = 4,
+  FA_ERR_HIP = 5                 /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/*
+ * fa_fwd -- dense batched attention (MHA or GQA), optional causal mask,
+ * optional LSE output.
+ *
+ *   q  [batch, seqlen_q, heads_q,  head_dim]   strides q_stride  = {batch, seq, head}
+ *   k  [batch, seqlen_k, heads_kv, head_dim]   strides k_stride
+ *   v  [batch, seqlen_k, heads_kv, head_dim]   strides v_stride
+ *   o  [batch, seqlen_q, heads_q,  head_dim]   strides o_stride  (written)
+ *   lse [batch, heads_q, seqlen_q] fp32, contiguous (written; may be NULL)
+ *
+ * dtype FA_F32 (fp32 in, fp32 out, fp32 MFMA) or FA_BF16 (bf16 in, bf16 out
+ * rounded to nearest-even, fp32 accumulation); head_dim 64 or 128.
+ * seqlen_q == 0 or batch == 0 is a no-op; seqlen_k == 0 writes O = 0 and
+ * LSE = -inf.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  fa_dtype dtype;
+  float scale;
+  int32_t causal;
+} fa_fwd_args;
+
+fa_status fa_fwd(const fa_fwd_args *args, void *stream);
+
+/*
+ * fa_fwd_varlen -- packed variable-length sequences, no padding tokens.
+ *
+ *   q  [total_tokens, heads_q,  head_dim]   strides q_stride = {token, head}
+ *   k,v[total_tokens, heads_kv, head_dim]
+ *   o  [total_tokens, heads_q,  head_dim]   (written)
+ *   lse [heads_q, total_tokens] fp32 contiguous (written; may be NULL)
+ *   cu_seqlens: DEVICE int32 [num_seqs + 1], cu[0] = 0, non-decreasing,
+ *     cu[num_seqs] = total_tokens; sequence s owns tokens [cu[s], cu[s+1]).
+ *   max_seqlen: a HOST-side upper bound on every sequence length (it sizes
+ *     the grid; the library never reads cu_seqlens on the host).  A sequence
+ *     longer than max_seqlen is processed only up to max_seqlen queries.
+ *
+ * A query sees only keys of its own sequence (causal in local positions
+ * when causal != 0).  dtype FA_BF16 only; head_dim 64 or 128.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens;
+  int32_t num_seqs, total_tokens, max_seqlen, heads_q, heads_kv, head_dim;
+  int64_t q_stride[2], k_stride[2], v_stride[2], o_stride[2];
+  fa_dtype dtype;
+  float scale;
+  int32_t causal;
+} fa_fwd_varlen_args;
+
+fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
+
+/*
+ * fa_decode_paged -- one query token per sequence over a paged KV pool
+ * (flash-decoding: the keys of each sequence are split across workgroups
+ * and the partial (m, l, o) states are merged by a second kernel).
+ *
+ *   q   [batch, heads_q, head_dim] bf16, strides q_stride = {batch, head}
+ *   k_pool, v_pool: bf16 block pools addressed with element strides
+ *       pool_stride = {block, head, token}; the default layout is
+ *       [num_blocks, heads_kv, block_size, head_dim].  Both pools share the
+ *       strides.
+ *   block_table: DEVICE int32 [batch, max_blocks_per_seq] (row stride
+ *       max_blocks_per_seq); logical key t of sequence b lives in block
+ *       block_table[b][t / block_size], slot t % block_size.  Entries past
+ *       ceil(seq_lens[b] / block_size) are never read.  Entries that are read
+ *       must lie in [0, num_blocks): the kernel does not check them.
+ *   seq_lens: DEVICE int32 [batch], each in [0, max_seq_len].
+ *   o   [batch, heads_q, head_dim] bf16, strides o_stride (written)
+ *   lse [batch, heads_q] fp32 contiguous (written; may be NULL)
+ *   max_seq_len: HOST-side upper bound on seq_lens (sizes the split grid),
+ *       at most max_blocks_per_seq * block_size.
+ *   num_splits: maximum number of key splits per sequence, 0 = library
+ *       choice.  Split boundaries depend only on logical token positions,
+ *       so a permuted pool gives bit-identical results.
+ *   workspace: DEVICE scratch of at least fa_decode_paged_workspace_size()
+ *       bytes, owned by the caller; contents on entry are ignored.
+ *
+ * Supported: bf16, head_dim 128, block_size 16, heads_q / heads_kv <= 8.
+ */
+typedef struct {
+  const void *q;
+  const void *k_pool, *v_pool;
+  int64_t pool_stride[3];
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  void *o;
+  float *lse;
+  int64_t q_stride[2], o_stride[2];
+  int32_t batch, heads_q, heads_kv, head_dim, block_size, max_blocks_per_seq, num_blocks,
+      max_seq_len;
+  float scale;
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+} fa_decode_paged_args;
+
+/* Bytes of workspace fa_decode_paged needs for these arguments (0 on invalid
+ * arguments).  Depends only on batch, heads_q, head_dim, max_seq_len,
+ * block_size and num_splits. */
+size_t fa_decode_paged_workspace_size(const fa_decode_paged_args *args);
+
+fa_status fa_decode_paged(const fa_decode_paged_args *args, void *stream);
+
+/* The number of key splits fa_decode_paged will use for these arguments. */
+int32_t fa_decode_paged_num_splits(const fa_decode_paged_args *args);
+
+/* Static text for a status code. */
+const char *fa_status_string(fa_status status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *fa_last_error(void);
+
+/* FA_ABI_VERSION of the loaded library. */
+int32_t fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_GFX950_H */

@@ -1,0 +1,230 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+* libfa_gfx950.so loads and exports every function include/fa.h declares;
+* the ctypes mirrors of the argument structs have the C layout (checked
+  against gcc's sizeof/offsetof of include/fa.h);
+* every invalid argument is rejected with its status before any launch, and
+  no-op calls return FA_OK without touching memory;
+* workspace and split sizing follow the documented rules.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_io_aware_tile_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa_gfx950.so is not built (python -m exact_io_aware_tile_amd.build)")
+    return fa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(fa.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True)
+    exported = {l.split()[-1] for l in out.stdout.splitlines() if " T " in l}
+    assert set(names) <= exported
+    # nothing else of the library's own leaks out under the fa_ prefix
+    assert {e for e in exported if e.startswith("fa_")} == set(names)
+
+
+def test_abi_version_and_strings(L):
+    assert L.fa_abi_version() == 1
+    for st in range(6):
+        assert L.fa_status_string(st)
+    assert L.fa_status_string(0) == b"ok"
+
+
+STRUCTS = {
+    "fa_fwd_args": fa.FwdArgs,
+    "fa_fwd_varlen_args": fa.FwdVarlenArgs,
+    "fa_decode_paged_args": fa.DecodePagedArgs,
+}
+
+
+def test_struct_layout_matches_header(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fa.h"', "int main(void) {"]
+    for cname, py in STRUCTS.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["return 0; }"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, py in STRUCTS.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def fwd_args(**kw):
+    a = fa.FwdArgs()
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = 1, 8, 8, 2, 2, 64
+    a.dtype, a.scale, a.causal = fa.FA_BF16, 0.125, 1
+    a.q = a.k = a.v = a.o = 0x1000
+    for arr in (a.q_stride, a.k_stride, a.v_stride, a.o_stride):
+        arr[:] = [8 * 2 * 64, 2 * 64, 64]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(heads_kv=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(batch=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(seqlen_k=-2), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SHAPE),
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(o=None), fa.FA_ERR_NULL_POINTER),
+    (dict(q=0x1002), fa.FA_ERR_BAD_SHAPE),
+    (dict(k_stride=[1024, 129, 64]), fa.FA_ERR_BAD_SHAPE),
+    (dict(v_stride=[1024, -128, 64]), fa.FA_ERR_BAD_SHAPE),
+])
+def test_fwd_rejects_before_launch(L, kw, status):
+    a = fwd_args(**kw)
+    assert L.fa_fwd(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_fwd_empty_is_noop(L):
+    for kw in (dict(batch=0), dict(seqlen_q=0)):
+        a = fwd_args(q=None, k=None, v=None, o=None, **kw)
+        assert L.fa_fwd(ctypes.byref(a), None) == fa.FA_OK
+        assert L.fa_last_error() == b""
+    assert L.fa_fwd(None, None) == fa.FA_ERR_NULL_POINTER
+
+
+def varlen_args(**kw):
+    a = fa.FwdVarlenArgs()
+    a.num_seqs, a.total_tokens, a.max_seqlen, a.heads_q, a.heads_kv, a.head_dim = 2, 10, 6, 2, 1, 64
+    a.dtype, a.scale, a.causal = fa.FA_BF16, 0.125, 1
+    a.q = a.k = a.v = a.o = a.cu_seqlens = 0x1000
+    for arr in (a.q_stride, a.o_stride):
+        arr[:] = [2 * 64, 64]
+    for arr in (a.k_stride, a.v_stride):
+        arr[:] = [64, 64]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=3, heads_kv=2), fa.FA_ERR_BAD_SHAPE),
+    (dict(num_seqs=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(cu_seqlens=None), fa.FA_ERR_NULL_POINTER),
+    (dict(q_stride=[100, 64]), fa.FA_ERR_BAD_SHAPE),
+    (dict(o=0x1008), fa.FA_ERR_BAD_SHAPE),
+])
+def test_varlen_rejects_before_launch(L, kw, status):
+    a = varlen_args(**kw)
+    assert L.fa_fwd_varlen(ctypes.byref(a), None) == status
+
+
+def test_varlen_empty_is_noop(L):
+    for kw in (dict(num_seqs=0), dict(max_seqlen=0), dict(total_tokens=0)):
+        a = varlen_args(q=None, k=None, v=None, o=None, cu_seqlens=None, **kw)
+        assert L.fa_fwd_varlen(ctypes.byref(a), None) == fa.FA_OK
+
+
+def decode_args(**kw):
+    a = fa.DecodePagedArgs()
+    a.batch, a.heads_q, a.heads_kv, a.head_dim, a.block_size = 4, 32, 8, 128, 16
+    a.max_blocks_per_seq, a.num_blocks, a.max_seq_len = 64, 200, 1000
+    a.scale, a.num_splits = 0.088, 0
+    a.q = a.k_pool = a.v_pool = a.block_table = a.seq_lens = a.o = a.workspace = 0x1000
+    a.pool_stride[:] = [8 * 16 * 128, 16 * 128, 128]
+    a.q_stride[:] = [32 * 128, 128]
+    a.o_stride[:] = [32 * 128, 128]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    if "workspace_bytes" not in kw:
+        a.workspace_bytes = 0
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=30), fa.FA_ERR_BAD_SHAPE),
+    (dict(heads_q=24), fa.FA_ERR_UNSUPPORTED),   # group 3
+    (dict(heads_kv=2), fa.FA_ERR_UNSUPPORTED),   # group 16
+    (dict(head_dim=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(block_size=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(max_seq_len=64 * 16 + 1), fa.FA_ERR_BAD_SHAPE),
+    (dict(batch=-3), fa.FA_ERR_BAD_SHAPE),
+    (dict(num_splits=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(block_table=None), fa.FA_ERR_NULL_POINTER),
+    (dict(workspace=None), fa.FA_ERR_NULL_POINTER),
+    (dict(pool_stride=[8 * 16 * 128, 16 * 128, 100]), fa.FA_ERR_BAD_SHAPE),
+    (dict(v_pool=0x1010 + 4), fa.FA_ERR_BAD_SHAPE),
+    (dict(), fa.FA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_rejects_before_launch(L, kw, status):
+    a = decode_args(**kw)
+    assert L.fa_decode_paged(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_decode_sizes(L):
+    a = decode_args(num_splits=4)
+    ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
+    assert ns == 4  # 1000 tokens in splits of 256
+    assert L.fa_decode_paged_workspace_size(ctypes.byref(a)) == 4 * 32 * 4 * (128 + 2) * 4
+    a = decode_args(num_splits=7, max_seq_len=1000)
+    ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
+    st = -(-(-(-1000 // 7)) // 16) * 16  # ceil(1000/7) rounded up to 16 = 144
+    assert ns == -(-1000 // st)
+    a = decode_args()  # auto: splits of 256..1024 tokens
+    ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
+    assert 1 <= ns <= -(-1000 // 256)
+    bad = decode_args(head_dim=64)
+    assert L.fa_decode_paged_workspace_size(ctypes.byref(bad)) == 0
+    assert L.fa_decode_paged_num_splits(ctypes.byref(bad)) == 0
+
+
+def test_decode_empty_batch_is_noop(L):
+    a = decode_args(batch=0, q=None, k_pool=None, v_pool=None, block_table=None, seq_lens=None,
+                    o=None, workspace=None)
+    assert L.fa_decode_paged(ctypes.byref(a), None) == fa.FA_OK
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.lib(str(tmp_path / "missing.so"))

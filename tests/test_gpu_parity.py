@@ -1,0 +1,337 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64 oracle.
+
+Tolerances: fp32 I/O max |dO| <= 1e-5; bf16 I/O max |dO| <= 2e-2 and mean
+|dO| <= 2e-3; max |dLSE| <= 1e-3 (natural log).  Inputs are the seeded
+generators of exact_io_aware_tile_amd.inputs; the oracle sees exactly the
+bytes the GPU sees.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_tile_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, None), "bf16": (2e-2, 2e-3)}
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_io_aware_tile_amd import fa
+    fa.lib()  # must load; no fallback exists
+    return fa
+
+
+def dev(a, dtype):
+    """Host array (float32, or uint16 bf16 bits) -> GPU tensor with the same bytes."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    tmax, tmean = TOL[dtype]
+    err = np.abs(o_gpu - o_ref)
+    assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
+    assert err.max() <= tmax, f"{what}: max |dO| = {err.max():.3e} > {tmax}"
+    if tmean is not None:
+        assert err.mean() <= tmean, f"{what}: mean |dO| = {err.mean():.3e} > {tmean}"
+    if lse_gpu is not None:
+        fin = np.isfinite(lse_ref)
+        np.testing.assert_array_equal(np.isfinite(lse_gpu), fin, err_msg=f"{what}: LSE finiteness")
+        np.testing.assert_array_equal(lse_gpu[~fin], lse_ref[~fin])
+        if fin.any():
+            e = np.abs(lse_gpu[fin] - lse_ref[fin]).max()
+            assert e <= LSE_TOL, f"{what}: max |dLSE| = {e:.3e}"
+
+
+def run_dense(fa, case, causal, rows=None):
+    dt = case["dtype"]
+    q, k, v = (dev(case[n], dt) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.dense(case["q"], case["k"], case["v"], causal=causal, rows=rows)
+    og = host(o).transpose(0, 2, 1, 3)  # [B, Hq, Nq, d]
+    lg = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        og = og.reshape(-1, og.shape[-1])[rows]
+        lg = lg.reshape(-1)[rows]
+    return og, lg, o_ref, lse_ref
+
+
+DENSE_SHAPES = [
+    # B, Nq, Nk, Hq, Hkv, d
+    (1, 1, 1, 1, 1, 64),
+    (2, 17, 17, 2, 2, 64),
+    (1, 63, 63, 2, 1, 128),
+    (1, 64, 64, 1, 1, 128),
+    (2, 65, 65, 4, 2, 64),
+    (1, 255, 255, 2, 2, 128),
+    (1, 300, 300, 3, 1, 64),
+    (1, 1000, 1000, 2, 2, 128),
+    (1, 17, 200, 2, 2, 128),   # fewer queries than keys (end-aligned causal)
+    (1, 200, 70, 2, 2, 64),    # more queries than keys: first rows see nothing when causal
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", DENSE_SHAPES)
+def test_dense_parity(gpu, shape, causal, dtype):
+    B, Nq, Nk, Hq, Hkv, d = shape
+    case = inputs.dense_case(100 + Nq + d, B, Nq, Nk, Hq, Hkv, d, dtype=dtype)
+    og, lg, o_ref, lse_ref = run_dense(gpu, case, causal)
+    check(og, lg, o_ref, lse_ref, dtype, f"{shape} causal={causal} {dtype}")
+
+
+def test_workload1_fp32(gpu):
+    case = inputs.workload(1)
+    og, lg, o_ref, lse_ref = run_dense(gpu, case, case["causal"])
+    check(og, lg, o_ref, lse_ref, "f32", "fp32 N=256 d=64")
+
+
+def test_worked_example_on_gpu(gpu):
+    """Row 1, 0.5, 2, 1.5 | 3, 0.2, 1, 2.5 from the merge-rule worked example on
+    the "FlashAttention" page of tachyon.techntrek.in: with q = 8 e0, k_j =
+    row_j e0 (scale 1/8) and V = identity, O is the softmax row and
+    exp(LSE - 3) is the merged l printed as 2.611."""
+    row = np.array([1.0, 0.5, 2.0, 1.5, 3.0, 0.2, 1.0, 2.5], dtype=np.float32)
+    d, n = 64, 8
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[0, 0, 0, 0] = 8.0
+    k = np.zeros((1, n, 1, d), np.float32)
+    k[0, :, 0, 0] = row
+    v = np.zeros((1, n, 1, d), np.float32)
+    v[0, np.arange(n), 0, np.arange(n)] = 1.0
+    o, lse = gpu.fa_fwd(dev(q, "f32"), dev(k, "f32"), dev(v, "f32"), causal=False, scale=0.125)
+    torch.cuda.synchronize()
+    w = host(o)[0, 0, 0, :n]
+    L = float(lse.cpu()[0, 0, 0])
+    assert abs(math.exp(L - 3.0) - 2.611) < 1e-3
+    assert abs(math.exp(L - 2.0) * w[:4].sum() - 2.198) < 1e-3
+    assert abs(math.exp(L - 3.0) * w[4:].sum() - 1.803) < 1e-3
+    o_ref, l_ref = oracle.dense(q, k, v, causal=False, scale=0.125)
+    np.testing.assert_allclose(w, o_ref[0, 0, 0, :n], atol=1e-6, rtol=0)
+    assert abs(L - l_ref[0, 0, 0]) < 1e-5
+    assert abs(w.sum() - 1.0) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_closed_forms_on_gpu(gpu, dtype):
+    B, N, H, d = 1, 300, 2, 128
+    case = inputs.dense_case(7, B, N, N, H, H, d, dtype=dtype)
+    ones = np.ones((B, N, H, d), np.float32)
+    v1 = inputs.f32_to_bf16(ones) if dtype == "bf16" else ones
+    q, k = dev(case["q"], dtype), dev(case["k"], dtype)
+    o, _ = gpu.fa_fwd(q, k, dev(v1, dtype), causal=True)
+    assert np.abs(host(o) - 1.0).max() <= TOL[dtype][0]
+    # q = 0: uniform weights, LSE = ln(i + 1) under the causal mask
+    zq = torch.zeros_like(q)
+    o, lse = gpu.fa_fwd(zq, k, dev(case["v"], dtype), causal=True)
+    torch.cuda.synchronize()
+    ln = np.log(np.arange(1, N + 1))
+    assert np.abs(lse.cpu().numpy()[0] - ln[None]).max() < 1e-4
+    vv = (inputs.bf16_to_f32(case["v"]) if dtype == "bf16" else case["v"]).astype(np.float64)
+    mean = np.cumsum(vv[0], axis=0) / np.arange(1, N + 1)[:, None, None]
+    assert np.abs(host(o)[0] - mean).max() <= TOL[dtype][0]
+
+
+def test_strided_views(gpu):
+    B, N, H, d = 2, 130, 2, 128
+    big = inputs.dense_case(8, B, N, N, 2 * H, 2 * H, d, dtype="bf16")
+    q = dev(big["q"], "bf16")[:, :, 1::2]  # head stride 2*d
+    k = dev(big["k"], "bf16")[:, :, :H]
+    v = dev(big["v"], "bf16")[:, :, H:]
+    out = torch.empty((B, N, 2 * H, d), dtype=torch.bfloat16, device="cuda")[:, :, ::2]
+    o, lse = gpu.fa_fwd(q, k, v, causal=True, out=out)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.dense(big["q"][:, :, 1::2], big["k"][:, :, :H], big["v"][:, :, H:], causal=True)
+    check(host(o).transpose(0, 2, 1, 3), lse.cpu().numpy().astype(np.float64), o_ref, l_ref, "bf16",
+          "strided")
+
+
+def test_empty_keys(gpu):
+    q = torch.randn(1, 5, 2, 64, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(1, 0, 2, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = gpu.fa_fwd(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def sample_rows(rng, B, H, N, n):
+    """Row ids (b*H + h)*N + i: random rows plus tile edges and the last row."""
+    ids = set(rng.integers(0, B * H * N, size=n).tolist())
+    for i in (0, 1, 63, 64, 127, 128, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1):
+        if 0 <= i < N:
+            ids.add(int(rng.integers(0, B * H)) * N + i)
+    return np.array(sorted(ids), dtype=np.int64)
+
+
+@pytest.mark.parametrize("wl", [2, 3])
+def test_prefill_workloads_sampled(gpu, wl):
+    case = inputs.workload(wl)
+    B, N, H = case["batch"], case["nq"], case["hq"]
+    rows = sample_rows(np.random.default_rng(wl), B, H, N, 384)
+    og, lg, o_ref, lse_ref = run_dense(gpu, case, case["causal"], rows=rows)
+    check(og, lg, o_ref, lse_ref, "bf16", f"workload {wl} sampled rows")
+
+
+def test_prefill_full_size_properties(gpu):
+    """At full size every output row is a convex combination of value rows
+    (inside their per-dimension range) and every LSE is finite."""
+    case = inputs.workload(3)
+    q, k, v = (dev(case[n], "bf16") for n in ("q", "k", "v"))
+    o, lse = gpu.fa_fwd(q, k, v, causal=True)
+    of = o.float()
+    assert torch.isfinite(of).all() and torch.isfinite(lse).all()
+    vf = v.float()
+    vmin = torch.cummin(vf, dim=1).values  # causal: keys 0..i
+    vmax = torch.cummax(vf, dim=1).values
+    slack = 1e-2
+    assert bool((of >= vmin - slack).all()) and bool((of <= vmax + slack).all())
+    # LSE >= the row's own diagonal score (that key is always visible)
+    diag = (q.float() * k.float()).sum(-1) / math.sqrt(case["d"])  # [B, N, H]
+    assert bool((lse.permute(0, 2, 1) >= diag - 1e-3).all())
+
+
+# --------------------------------------------------------------------------
+# packed variable-length
+# --------------------------------------------------------------------------
+def run_varlen(fa, case, causal, rows=None):
+    q, k, v = (dev(case[n], case["dtype"]) for n in ("q", "k", "v"))
+    cu = torch.from_numpy(case["cu_seqlens"]).cuda()
+    o, lse = fa.fa_fwd_varlen(q, k, v, cu, case["max_seqlen"], causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.varlen(case["q"], case["k"], case["v"], case["cu_seqlens"], causal=causal,
+                                   rows=rows)
+    og = host(o).transpose(1, 0, 2)  # [Hq, T, d]
+    lg = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        og = og.reshape(-1, og.shape[-1])[rows]
+        lg = lg.reshape(-1)[rows]
+    return og, lg, o_ref, lse_ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_parity(gpu, d, causal, dtype):
+    lens = [1, 130, 0, 64, 257, 7, 128]
+    case = inputs.varlen_case(200 + d, lens, 4, 2, d, dtype=dtype)
+    og, lg, o_ref, lse_ref = run_varlen(gpu, case, causal)
+    check(og, lg, o_ref, lse_ref, dtype, f"varlen d={d} causal={causal}")
+
+
+def test_varlen_workload_sampled(gpu):
+    case = inputs.workload(4)
+    T, H = case["total"], case["hq"]
+    rng = np.random.default_rng(4)
+    rows = set(rng.integers(0, H * T, size=384).tolist())
+    cu = case["cu_seqlens"]
+    for s in range(len(cu) - 1):  # first and last token of every sequence
+        for t in (cu[s], cu[s + 1] - 1):
+            rows.add(int(rng.integers(0, H)) * T + int(t))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    og, lg, o_ref, lse_ref = run_varlen(gpu, case, True, rows=rows)
+    check(og, lg, o_ref, lse_ref, "bf16", "varlen workload sampled rows")
+
+
+def test_varlen_matches_dense_per_sequence(gpu):
+    lens = [100, 300, 5]
+    case = inputs.varlen_case(9, lens, 2, 2, 128, dtype="bf16")
+    q, k, v = (dev(case[n], "bf16") for n in ("q", "k", "v"))
+    cu = torch.from_numpy(case["cu_seqlens"]).cuda()
+    o, lse = gpu.fa_fwd_varlen(q, k, v, cu, max(lens), causal=True)
+    for s, L in enumerate(lens):
+        a, b = case["cu_seqlens"][s], case["cu_seqlens"][s + 1]
+        od, ld = gpu.fa_fwd(q[None, a:b], k[None, a:b], v[None, a:b], causal=True)
+        # identical tiling of identical data: identical bits
+        assert torch.equal(o[a:b], od[0])
+        assert torch.equal(lse[:, a:b], ld[0])
+
+
+# --------------------------------------------------------------------------
+# paged decode
+# --------------------------------------------------------------------------
+def decode_gpu(fa, case, num_splits=0, k_pool=None, v_pool=None, table=None):
+    q = dev(case["q"], "bf16")
+    kp = dev(case["k_pool"], "bf16") if k_pool is None else k_pool
+    vp = dev(case["v_pool"], "bf16") if v_pool is None else v_pool
+    bt = torch.from_numpy(case["block_table"]).cuda() if table is None else table
+    sl = torch.from_numpy(case["seq_lens"]).cuda()
+    maxlen = int(case["seq_lens"].max(initial=0))
+    o, lse = fa.fa_decode_paged(q, kp, vp, bt, sl, maxlen, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_decode_parity(gpu, group, num_splits):
+    lens = [1, 16, 17, 100, 0, 333, 48, 1000]
+    hkv = 2
+    case = inputs.paged_case(300 + group, lens, hkv * group, hkv, 128, pad_blocks=2)
+    o, lse = decode_gpu(gpu, case, num_splits=num_splits)
+    o_ref, lse_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                         case["seq_lens"])
+    check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+          f"decode group={group} splits={num_splits}")
+
+
+def test_decode_paged_equals_contiguous_bitwise(gpu):
+    lens = [5000, 17, 1024, 333, 4097]
+    case = inputs.paged_case(310, lens, 32, 8, 128)
+    o1, l1 = decode_gpu(gpu, case, num_splits=0)
+    # the same logical keys, blocks laid out in table order, identity table
+    bt = case["block_table"]
+    order = np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(lens)]).astype(np.int64)
+    idx = torch.from_numpy(order).cuda()
+    kp = dev(case["k_pool"], "bf16").index_select(0, idx)
+    vp = dev(case["v_pool"], "bf16").index_select(0, idx)
+    ident = np.full_like(bt, -1)
+    pos = 0
+    for b, L in enumerate(lens):
+        nb = (L + 15) // 16
+        ident[b, :nb] = np.arange(pos, pos + nb)
+        pos += nb
+    o2, l2 = decode_gpu(gpu, case, num_splits=0, k_pool=kp, v_pool=vp,
+                        table=torch.from_numpy(ident).cuda())
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+
+
+def test_decode_token_major_pool(gpu):
+    lens = [40, 300]
+    case = inputs.paged_case(320, lens, 8, 2, 128)
+    o1, l1 = decode_gpu(gpu, case)
+    kt = dev(np.ascontiguousarray(case["k_pool"].transpose(0, 2, 1, 3)), "bf16").transpose(1, 2)
+    vt = dev(np.ascontiguousarray(case["v_pool"].transpose(0, 2, 1, 3)), "bf16").transpose(1, 2)
+    o2, l2 = decode_gpu(gpu, case, k_pool=kt, v_pool=vt)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_workload_sampled(gpu):
+    case = inputs.workload(5)
+    o, lse = decode_gpu(gpu, case)
+    B, H = case["q"].shape[:2]
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.integers(0, B * H, size=96),
+                                     [int(np.argmax(case["seq_lens"])) * H, int(np.argmin(case["seq_lens"])) * H]]))
+    o_ref, lse_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                         case["seq_lens"], rows=rows)
+    og = host(o).reshape(B * H, -1)[rows]
+    lg = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
+    check(og, lg, o_ref, lse_ref, "bf16", "decode workload sampled")
