@@ -47,9 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "varlen", "copy"], default=None,
-                    help="run one workload only (for profiler runs); 'copy' runs a plain 1 GiB "
-                         "device copy used to calibrate the HBM byte counters")
+    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "copy"],
+                    default=None,
+                    help="run only these workloads and print one JSON line each (for profiler "
+                         "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
+                         "HBM byte counters")
     return ap.parse_args()
 
 
@@ -225,27 +227,30 @@ def main():
     fa.lib()
     torch.cuda.set_device(0)
 
-    if args.only == "copy":
-        run_copy(torch, args.steps)
-        return
+    only = set(args.only or [])
+
+    def want(name, default=True):
+        return name in only if only else default
 
     out = {}
-    if args.only in (None, "prefill"):
+    if want("prefill"):
         case = inputs.workload(2)
         res = run_prefill(fa, case, args.steps, args.warmup, torch, np, "prefill")
         out["prefill"] = (case, res)
-    if args.only == "long" or (args.only is None and not args.no_extra):
+    if want("long", not args.no_extra):
         case = inputs.workload(3)
         out["long"] = (case, run_prefill(fa, case, max(5, args.steps // 5), max(2, args.warmup // 5), torch, np,
                                          "prefill"))
-    if args.only == "varlen" or (args.only is None and not args.no_extra):
+    if want("varlen", not args.no_extra):
         case = inputs.workload(4)
         out["varlen"] = (case, run_varlen(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2), torch, np))
-    if args.only == "decode" or (args.only is None and not args.no_decode):
+    if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np))
+    if want("copy", False):
+        run_copy(torch, args.steps)
 
-    if args.only is not None:
+    if only:
         for k, (case, res) in out.items():
             print(json.dumps({"workload": case["name"], **{a: b for a, b in res.items() if a != "roofline"},
                               "roofline": res["roofline"]}))

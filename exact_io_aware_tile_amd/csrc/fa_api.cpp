@@ -123,7 +123,9 @@ FA_EXPORT fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
     return fail(FA_ERR_BAD_SHAPE, "fa_fwd: scale must be positive and finite");
   if (a->batch == 0 || a->seqlen_q == 0) return ok();
-  if (!a->q || !a->k || !a->v || !a->o) return fail(FA_ERR_NULL_POINTER, "fa_fwd: q, k, v and o are required");
+  if (!a->q || !a->o) return fail(FA_ERR_NULL_POINTER, "fa_fwd: q and o are required");
+  if (a->seqlen_k > 0 && (!a->k || !a->v))
+    return fail(FA_ERR_NULL_POINTER, "fa_fwd: k and v are required when seqlen_k > 0");
   const int64_t e16 = a->dtype == FA_BF16 ? 8 : 4;
   if (!strides_ok(a->q_stride, 3, e16) || !strides_ok(a->k_stride, 3, e16) || !strides_ok(a->v_stride, 3, e16) ||
       !strides_ok(a->o_stride, 3, e16))

@@ -15,17 +15,17 @@
 // page of tachyon.techntrek.in ("For engineers / Show the maths"):
 // m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2, and o rescales the same way.
 //
-// gfx950 mapping of the split kernel: one wave per (sequence, kv head, split).
-// A 16-token x 128-dim bf16 block is 4 KB; the wave reads it with four
-// coalesced 16-byte loads per lane (lane l, load a: token 4a + l/16, dims
-// 8*(l%16) .. +7), prefetching the next block's K and V while it computes the
-// current one.  The G query heads of the group share every load.  Partial dot
-// products are summed over the 16 lanes of a token with a reduce-scatter, so
-// afterwards each lane owns the complete score of one (token, head) pair;
-// the block's weights are exchanged through a 16 x G LDS table for the P.V
-// step.  Split boundaries are multiples of the block size and depend only on
-// logical token positions, so the result does not depend on where the blocks
-// sit in the pool.
+// gfx950 mapping of the split kernel: one wave per (sequence, kv head, split),
+// no LDS and no barriers.  A 16-token x 128-dim bf16 block of one kv head is
+// 4 KB; every 16-byte load of the wave covers 8 token rows x 128 contiguous
+// bytes.  The G query heads of the group share every load (GQA).  q.k uses
+// v_dot2_f32_bf16 on the raw bf16 pairs, and a token's partial dot products
+// are summed across its 8 lanes with DPP moves.  Split boundaries are
+// multiples of the block size and depend only on logical token positions, and
+// nothing in the arithmetic depends on where a block sits in the pool, so a
+// permuted pool gives bit-identical results.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -46,13 +46,50 @@ __device__ __forceinline__ void unpack8(const uint4 w, float (&f)[8]) {
   f[7] = bf16_hi(w.w);
 }
 
+// Cross-lane moves inside a row of 16 lanes (DPP, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowRor8 = 0x128;
+
+// Sum over the 8 lanes that share lane bits 3..5 (one token row of a block).
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_mov<kQuadXor1>(x);
+  x += dpp_mov<kQuadXor2>(x);
+  x += dpp_mov<kRowHalfMirror>(x);  // lane i <-> 7 - i: the other quad of the 8
+  return x;
+}
+
+// 8 bf16 of a and b: acc + sum a_i * b_i (fp32 accumulation, v_dot2_f32_bf16).
+__device__ __forceinline__ float dot8(const uint4 a, const uint4 b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
+  return acc;
+}
+
+// One block's K and V as this lane holds them: tokens t0 and t0 + 8, dims
+// 8c..8c+7 and 64+8c..64+8c+7.
+struct KV {
+  uint4 k[2][2];
+  uint4 v[2][2];
+};
+
+// Split kernel.  Lane l = 8*t0 + c owns tokens t0 and t0 + 8 of every block
+// and the 16 dims {8c + e, 64 + 8c + e}; the 8 lanes of a token row read its
+// 256 bytes with two fully coalesced 128-byte runs.  Each lane runs the
+// recurrence on its own token stream (tokens t0, t0 + 8, t0 + 16, ...) with
+// its own (m, l, o) per query head -- the keys of the split are split once
+// more across the 8 token slots of the wave -- and the 8 slot states are
+// merged with the same rule at the end of the split.  Three K/V buffers keep
+// two blocks in flight while one is being consumed.
 template <int G>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
-  constexpr int HPL = G >= 4 ? G / 4 : 1;  // heads per lane after the reduction
-  constexpr int DUP = G >= 4 ? 1 : 4 / G;  // lanes that hold the same (token, head)
-  constexpr int NV = 4 * G;                // partial dot products per lane
-  __shared__ __attribute__((aligned(16))) float pl[kBlock][G];
-
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
@@ -66,176 +103,164 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) 
   const int blk0 = t_begin / kBlock;
   const int blk1 = (t_end + kBlock - 1) / kBlock;
 
-  const int sub = lane >> 4;
-  const int d8 = (lane & 15) * 8;
-  const int my_tok = 4 * ((lane >> 2) & 3) + sub;
-  const int hb = ((lane & 3) / DUP) * HPL;
+  const int c = lane & 7;
+  const int t0 = lane >> 3;
 
-  float qf[G][8];
+  uint4 qv[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      qv[h][i] = *(const uint4*)((const uint16_t*)p.q + (int64_t)b * p.q_bs + (int64_t)(g * G + h) * p.q_hs +
+                                 64 * i + 8 * c);
+
+  float o[G][2][8];
+  float m[G], l[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const uint4 w = *(const uint4*)((const uint16_t*)p.q + (int64_t)b * p.q_bs +
-                                    (int64_t)(g * G + h) * p.q_hs + d8);
-    unpack8(w, qf[h]);
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][i][e] = 0.f;
   }
 
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  float m_run[HPL], l_run[HPL];
-#pragma unroll
-  for (int e = 0; e < HPL; ++e) {
-    m_run[e] = -INFINITY;
-    l_run[e] = 0.f;
-  }
-
-  const uint16_t* __restrict__ kpool = (const uint16_t*)p.k_pool + (int64_t)g * p.p_hs + d8;
-  const uint16_t* __restrict__ vpool = (const uint16_t*)p.v_pool + (int64_t)g * p.p_hs + d8;
+  const uint16_t* __restrict__ kbase = (const uint16_t*)p.k_pool + (int64_t)g * p.p_hs + 8 * c;
+  const uint16_t* __restrict__ vbase = (const uint16_t*)p.v_pool + (int64_t)g * p.p_hs + 8 * c;
   const int32_t* __restrict__ bt = p.block_table + (int64_t)b * p.max_blocks;
-  const float c = p.scale_log2;
+  const float cs = p.scale_log2;
 
-  uint4 kc[4], vc[4];
-  auto load = [&](int blk, uint4 (&kd)[4], uint4 (&vd)[4]) {
-    const int64_t base = (int64_t)bt[blk] * p.p_bs;
+  // Loads past the split's last block re-read that block (it is in cache);
+  // their tokens are masked when processed.
+  auto issue = [&](KV& B, int blk) {
+    const int bb = blk < blk1 ? blk : blk1 - 1;
+    const int64_t base = (int64_t)bt[bb] * p.p_bs;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int64_t off = base + (int64_t)(4 * a + sub) * p.p_ts;
-      kd[a] = *(const uint4*)(kpool + off);
-      vd[a] = *(const uint4*)(vpool + off);
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t off = base + (int64_t)(t0 + 8 * a) * p.p_ts + 64 * i;
+        B.k[a][i] = *(const uint4*)(kbase + off);
+        B.v[a][i] = *(const uint4*)(vbase + off);
+      }
+  };
+
+  // One block through the recurrence.  TAIL masks tokens at or past t_end
+  // (only the sequence's last block can hold such tokens).
+  auto process = [&](const KV& B, int blk, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const int tok0 = blk * kBlock;
+    const bool ok0 = !TAIL || tok0 + t0 < t_end;
+    const bool ok1 = !TAIL || tok0 + t0 + 8 < t_end;
+    float s[2][G];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[a][h] = sum8(dot8(qv[h][1], B.k[a][1], dot8(qv[h][0], B.k[a][0], 0.f)));
+    float v0[2][8], v1[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      unpack8(B.v[0][i], v0[i]);
+      unpack8(B.v[1][i], v1[i]);
+      if (TAIL) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v0[i][e] = ok0 ? v0[i][e] : 0.f;
+          v1[i][e] = ok1 ? v1[i][e] : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float x0 = ok0 ? s[0][h] : -INFINITY;
+      const float x1 = ok1 ? s[1][h] : -INFINITY;
+      const float m_new = fmaxf(m[h], fmaxf(x0, x1) * cs);
+      const float mu = (!TAIL || m_new != -INFINITY) ? m_new : 0.f;
+      const float alpha = exp2_fast(m[h] - mu);
+      const float p0 = exp2_fast(__builtin_fmaf(x0, cs, -mu));
+      const float p1 = exp2_fast(__builtin_fmaf(x1, cs, -mu));
+      l[h] = __builtin_fmaf(alpha, l[h], p0 + p1);
+      m[h] = m_new;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[h][i][e] = __builtin_fmaf(p1, v1[i][e], __builtin_fmaf(p0, v0[i][e], o[h][i][e] * alpha));
     }
   };
-  load(blk0, kc, vc);
-
-  for (int blk = blk0; blk < blk1; ++blk) {
-    uint4 kn[4], vn[4];
-    if (blk + 1 < blk1) load(blk + 1, kn, vn);
-    const int tok0 = blk * kBlock;
-
-    // Partial q.k over this lane's 8 dims: x[a*G + h] for token 4a + sub.
-    float x[NV];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      float kf[8];
-      unpack8(kc[a], kf);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = __builtin_fmaf(qf[h][e], kf[e], s);
-        x[a * G + h] = s;
-      }
+  // Blocks wholly inside the split take the unmasked path; blocks past the
+  // split's end (the ring's overrun) are skipped.  The branch is uniform.
+  auto step = [&](const KV& B, int blk) {
+    if (blk * kBlock + kBlock <= t_end) {
+      process(B, blk, std::false_type{});
+    } else if (blk < blk1) {
+      process(B, blk, std::true_type{});
     }
-    // Reduce-scatter over the 16 lanes of a token row: each stage keeps half
-    // of the values (the half picked by one lane bit) and adds the partner's.
+  };
+
+  // The scheduling barriers keep each ring refill where it is written, two
+  // blocks ahead of its use, instead of letting the scheduler sink the loads
+  // next to their consumers.
+  KV A, B, C;
+  issue(A, blk0);
+  issue(B, blk0 + 1);
+  issue(C, blk0 + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int blk = blk0; blk < blk1; blk += 3) {
+    step(A, blk);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(A, blk + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    step(B, blk + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(B, blk + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    step(C, blk + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(C, blk + 5);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Merge the 8 token-slot states (lane bits 3..5) pairwise.
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int M = 8 >> st;
-      const int cnt = NV >> st;
-      if (cnt >= 2) {
-        const bool up = (lane & M) != 0;
+  for (int st = 0; st < 3; ++st) {
+    const int mask = 8 << st;
 #pragma unroll
-        for (int j = 0; j < cnt / 2; ++j) {
-          const float keep = up ? x[cnt / 2 + j] : x[j];
-          const float send = up ? x[j] : x[cnt / 2 + j];
-          x[j] = keep + __shfl_xor(send, M, 64);
+    for (int h = 0; h < G; ++h) {
+      const float mo = st == 0 ? dpp_mov<kRowRor8>(m[h]) : __shfl_xor(m[h], mask, 64);
+      const float lo = st == 0 ? dpp_mov<kRowRor8>(l[h]) : __shfl_xor(l[h], mask, 64);
+      const float M = fmaxf(m[h], mo);
+      const float mu = M == -INFINITY ? 0.f : M;
+      const float w = exp2_fast(m[h] - mu);
+      const float wo = exp2_fast(mo - mu);
+      l[h] = w * l[h] + wo * lo;
+      m[h] = M;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float oo = st == 0 ? dpp_mov<kRowRor8>(o[h][i][e]) : __shfl_xor(o[h][i][e], mask, 64);
+          o[h][i][e] = w * o[h][i][e] + wo * oo;
         }
-      } else {
-        x[0] += __shfl_xor(x[0], M, 64);
-      }
-    }
-    // x[e] is now the full score of (my_tok, hb + e).
-    const bool valid = tok0 + my_tok < t_end;
-    float alpha[HPL];
-#pragma unroll
-    for (int e = 0; e < HPL; ++e) {
-      const float s = valid ? x[e] : -INFINITY;
-      float tmax = s;
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 4, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[e], tmax * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[e] = exp2_fast(m_run[e] - m_use);
-      const float pe = exp2_fast(__builtin_fmaf(s, c, -m_use));
-      l_run[e] = alpha[e] * l_run[e] + pe;
-      m_run[e] = m_new;
-      if (lane % DUP == 0) pl[my_tok][hb + e] = pe;
-    }
-    __syncthreads();
-    // Correct the accumulators of every head (alpha is uniform per head).
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float ah = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[h % HPL]), (h / HPL) * DUP));
-      if (ah != 1.f) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
-      }
-    }
-    // P.V for this lane's four tokens and 8 dims.
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t = 4 * a + sub;
-      float vf[8];
-      unpack8(vc[a], vf);
-      if (tok0 + t >= t_end) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = 0.f;
-      }
-      float pw[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pw[h] = pl[t][h];
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(pw[h], vf[e], acc[h][e]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      kc[a] = kn[a];
-      vc[a] = vn[a];
     }
   }
 
-  // Sum l over the 16 tokens of a head and o over the 4 token sub-rows.
-#pragma unroll
-  for (int e = 0; e < HPL; ++e) {
-    float l = l_run[e];
-    l += __shfl_xor(l, 4, 64);
-    l += __shfl_xor(l, 8, 64);
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    l_run[e] = l;
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[h][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[h][e] = v;
-    }
-
-  const int64_t row0 = ((int64_t)b * p.heads_q + (int64_t)g * G) * p.num_splits + split;
-  if (sub == 0) {
+  if (t0 == 0) {
+    const int64_t row0 = ((int64_t)b * p.heads_q + (int64_t)g * G) * p.num_splits + split;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float* dst = p.ws_o + (row0 + (int64_t)h * p.num_splits) * kD + d8;
-      *(float4*)dst = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *(float4*)(dst + 4) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-  }
-  if (lane < 4 && lane % DUP == 0) {
+      float* dst = p.ws_o + (row0 + (int64_t)h * p.num_splits) * kD + 8 * c;
 #pragma unroll
-    for (int e = 0; e < HPL; ++e) {
-      float* ml = p.ws_ml + (row0 + (int64_t)(hb + e) * p.num_splits) * 2;
-      ml[0] = m_run[e];
-      ml[1] = l_run[e];
+      for (int i = 0; i < 2; ++i) {
+        *(float4*)(dst + 64 * i) = make_float4(o[h][i][0], o[h][i][1], o[h][i][2], o[h][i][3]);
+        *(float4*)(dst + 64 * i + 4) = make_float4(o[h][i][4], o[h][i][5], o[h][i][6], o[h][i][7]);
+      }
+      if (c == 0) {
+        float* ml = p.ws_ml + (row0 + (int64_t)h * p.num_splits) * 2;
+        ml[0] = m[h];
+        ml[1] = l[h];
+      }
     }
   }
 }

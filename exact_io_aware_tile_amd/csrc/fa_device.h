@@ -40,8 +40,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Value held by lane (l ^ 32) -- the other half of a 64-wide wave.
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// max / sum of x over lanes l and l ^ 32 (the two halves of a wave), via
+// v_permlane32_swap: swapping a register with itself leaves {x[l], x[l^32]}
+// in the two results on every lane, in some order.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;

@@ -40,6 +40,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 static_assert(kBr == kFwdRowsPerTile, "host tiling must match");
 constexpr int kBc = 64;           // keys per tile
+constexpr float kLazyLog2 = 8.f;  // max growth (base 2) tolerated before correcting o and l
 
 template <int D>
 struct Geometry {
@@ -49,7 +50,12 @@ struct Geometry {
   static constexpr int vElems = D * vStride;
   static constexpr int kChunks = kBc * D / 8 / kThreads;  // 16-byte K chunks per thread
   static constexpr int vKeys = kBc * D / 8 / kThreads;    // keys per thread in the V transpose
-  static constexpr int vGroups = D / 8;                   // 8-wide d groups per key
+  static constexpr int vKeyGroups = kBc / vKeys;          // key groups per tile
+  // Thread t transposes keys vKeys*(t % vKeyGroups) .. +vKeys-1 of dims
+  // 8*(t / vKeyGroups) .. +7.  Consecutive lanes take consecutive key groups
+  // of the same V^T rows, so each LDS write instruction covers whole rows
+  // (no bank conflicts); the V^T row pitch of 34 dwords keeps the reads of
+  // 16 consecutive rows on distinct banks.
 };
 
 template <int D, bool CAUSAL>
@@ -133,22 +139,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p
   // Global -> register staging of one K/V tile, then register -> LDS.
   uint4 kreg[G::kChunks];
   uint4 vreg[G::vKeys];
+  // Rows past the end of the keys are zero-filled, so masked weights never
+  // meet stale values; tiles wholly inside the keys take the unguarded path
+  // (a uniform branch).
+  const int kgrp = tid % G::vKeyGroups;
+  const int vcol = (tid / G::vKeyGroups) * 8;
   auto gload = [&](int tile) {
     const int k0 = tile * kBc;
+    if (k0 + kBc <= nk) {
 #pragma unroll
-    for (int i = 0; i < G::kChunks; ++i) {
-      const int c = i * kThreads + tid;
-      const int r = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      const int key = k0 + r;
-      kreg[i] = key < nk ? *(const uint4*)(kg + (int64_t)key * p.k_ss + col) : make_uint4(0, 0, 0, 0);
-    }
-    const int kgrp = tid / G::vGroups;
-    const int col = (tid % G::vGroups) * 8;
+      for (int i = 0; i < G::kChunks; ++i) {
+        const int c = i * kThreads + tid;
+        kreg[i] = *(const uint4*)(kg + (int64_t)(k0 + c / (D / 8)) * p.k_ss + (c % (D / 8)) * 8);
+      }
 #pragma unroll
-    for (int i = 0; i < G::vKeys; ++i) {
-      const int key = k0 + kgrp * G::vKeys + i;
-      vreg[i] = key < nk ? *(const uint4*)(vg + (int64_t)key * p.v_ss + col) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < G::vKeys; ++i)
+        vreg[i] = *(const uint4*)(vg + (int64_t)(k0 + kgrp * G::vKeys + i) * p.v_ss + vcol);
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::kChunks; ++i) {
+        const int c = i * kThreads + tid;
+        const int key = k0 + c / (D / 8);
+        kreg[i] = key < nk ? *(const uint4*)(kg + (int64_t)key * p.k_ss + (c % (D / 8)) * 8)
+                           : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < G::vKeys; ++i) {
+        const int key = k0 + kgrp * G::vKeys + i;
+        vreg[i] = key < nk ? *(const uint4*)(vg + (int64_t)key * p.v_ss + vcol) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -160,8 +179,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p
       *(uint4*)&ks[buf][r * G::kStride + col] = kreg[i];
     }
     // Transpose: thread holds vKeys keys x 8 d; write 8 rows of V^T.
-    const int kgrp = tid / G::vGroups;
-    const int col = (tid % G::vGroups) * 8;
     const uint32_t* w32 = (const uint32_t*)vreg;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -172,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p
         const uint32_t c = w32[(i + 1) * 4 + (e >> 1)];
         packed[i / 2] = (e & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
       }
-      uint16_t* dst = &vt[buf][(col + e) * G::vStride + kgrp * G::vKeys];
+      uint16_t* dst = &vt[buf][(vcol + e) * G::vStride + kgrp * G::vKeys];
       if constexpr (G::vKeys == 4) {
         *(uint2*)dst = make_uint2(packed[0], packed[1]);
       } else {
@@ -188,10 +205,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p
   float l_run = 0.f;        // this half-wave's share of the running sum
   const float c = p.scale_log2;
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  // The prologue runs even when no tile is visible (it only reads in-bounds
+  // rows): waiting here for the first tile also retires the Q loads on every
+  // path into the loop, so the loop never waits on them again.
+  gload(0);
+  lstore(0);
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
@@ -224,32 +242,42 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p
           }
       }
       // Online softmax update for this lane's row.
-      float tmax = sacc[0][0];
+      // Row max: a 4-way tree of max3 chains, then the other half-wave.
+      float mx[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int t = 0; t < 4; ++t) {
+        mx[t] = fmaxf(sacc[t >> 1][8 * (t & 1)], sacc[t >> 1][8 * (t & 1) + 1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
-      tmax = fmaxf(tmax, other_half(tmax));
+        for (int r = 2; r < 8; ++r) mx[t] = fmaxf(mx[t], sacc[t >> 1][8 * (t & 1) + r]);
+      }
+      float tmax = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+      // Lazy correction: the reference max m_run moves (and o, l are scaled
+      // by alpha = 2^(m_run - m_new)) only when some row of the wave sees its
+      // max grow by more than kLazyLog2; otherwise the weights are taken
+      // against the slightly stale reference, so p <= 2^kLazyLog2.  Any
+      // reference gives the same o / l; this one keeps the correction off
+      // the common path.
       const float m_new = fmaxf(m_run, tmax * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float psum = 0.f;
+      if (__any(m_new > m_run + kLazyLog2)) {
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -m_use));
           sacc[kb][r] = pv;
-          psum += pv;
+          ps[r & 3] += pv;
         }
-      l_run = alpha * l_run + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       // O^T += V^T P^T over four 16-key chunks.  Contraction slot j of lane
       // half hi is key 16*kc + 4*hi + j (j < 4) or 16*kc + 8 + 4*hi + (j-4):
       // exactly the keys this lane's score registers 8*(kc%2) .. +7 hold.
@@ -278,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdParams p
   }
 
   // Epilogue: O = o / l, LSE = (m + log2 l) * ln 2.
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = sum_halves(l_run);
   if (row < nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = (uint16_t*)p.o + o_base + (int64_t)row * p.o_ss;

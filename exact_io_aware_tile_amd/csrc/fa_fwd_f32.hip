@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
-      tmax = fmaxf(tmax, other_half(tmax));
+      tmax = max_halves(tmax);
       const float m_new = fmaxf(m_run, tmax * c);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2_fast(m_run - m_use);
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdParams p) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = sum_halves(l_run);
   if (row < nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* orow = (float*)p.o + o_base + (int64_t)row * p.o_ss;

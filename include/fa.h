@@ -80,7 +80,7 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
  * dtype FA_F32 (fp32 in, fp32 out, fp32 MFMA) or FA_BF16 (bf16 in, bf16 out
  * rounded to nearest-even, fp32 accumulation); head_dim 64 or 128.
  * seqlen_q == 0 or batch == 0 is a no-op; seqlen_k == 0 writes O = 0 and
- * LSE = -inf.
+ * LSE = -inf (k and v may then be NULL).
  */
 typedef struct {
   const void *q, *k, *v;
@@ -109,7 +109,8 @@ fa_status fa_fwd(const fa_fwd_args *args, void *stream);
  *     longer than max_seqlen is processed only up to max_seqlen queries.
  *
  * A query sees only keys of its own sequence (causal in local positions
- * when causal != 0).  dtype FA_BF16 only; head_dim 64 or 128.
+ * when causal != 0); an empty sequence writes nothing.  dtype FA_BF16 or
+ * FA_F32; head_dim 64 or 128.
  */
 typedef struct {
   const void *q, *k, *v;
