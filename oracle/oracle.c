@@ -6,10 +6,9 @@
  * GPU library and must never be used as a fallback for it.
  *
  * What it computes is the textbook definition that the tiled method reaches
- * exactly up to float reassociation ("S12 FlashAttention",
- * llminference.xinbetween.com, sections "Motivation / The problem" and the
- * "What this unlocks beyond speed" tile "not an approximation"): for one query
- * row i of one head,
+ * exactly, up to the order of floating-point additions ("S12 FlashAttention",
+ * llminference.xinbetween.com, sections "Motivation / The problem" and "What
+ * this unlocks beyond speed"): for one query row i of one head,
  *
  *     s_j   = scale * sum_c q[i][c] * k[j][c]        for every visible key j
  *     M     = max_j s_j
