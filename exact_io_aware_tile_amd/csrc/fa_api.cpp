@@ -133,7 +133,12 @@ FA_EXPORT fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
                 (long long)e16);
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return fail(FA_ERR_BAD_SHAPE, "fa_fwd: q, k, v, o must be 16-byte aligned");
-  const int64_t qtiles = (a->seqlen_q + fa::kFwdRowsPerTile - 1) / fa::kFwdRowsPerTile;
+  if (a->dtype == FA_BF16 &&
+      (a->k_stride[1] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[1] > fa::kFwdMaxKvRowStrideBf16))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: bf16 k/v row strides above %lld elements",
+                (long long)fa::kFwdMaxKvRowStrideBf16);
+  const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
+  const int64_t qtiles = (a->seqlen_q + rows - 1) / rows;
   if (qtiles * a->heads_q * a->batch > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "fa_fwd: grid too large");
 
   fa::FwdParams p{};
@@ -186,7 +191,12 @@ FA_EXPORT fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
                 (long long)e16);
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
     return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: q, k, v, o must be 16-byte aligned");
-  const int64_t qtiles = (a->max_seqlen + fa::kFwdRowsPerTile - 1) / fa::kFwdRowsPerTile;
+  if (a->dtype == FA_BF16 &&
+      (a->k_stride[0] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[0] > fa::kFwdMaxKvRowStrideBf16))
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: bf16 k/v token strides above %lld elements",
+                (long long)fa::kFwdMaxKvRowStrideBf16);
+  const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
+  const int64_t qtiles = (a->max_seqlen + rows - 1) / rows;
   if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
     return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: grid too large");
 

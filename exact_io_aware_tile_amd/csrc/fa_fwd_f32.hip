@@ -18,7 +18,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;
-static_assert(kBr == kFwdRowsPerTile, "host tiling must match");
+static_assert(kBr == kFwdRowsPerTileF32, "host tiling must match");
 constexpr int kBc = 64;
 
 template <int D, bool CAUSAL>

@@ -7,8 +7,12 @@
 
 namespace fa {
 
-// Query rows handled by one prefill workgroup (both dtypes).
-constexpr int kFwdRowsPerTile = 128;
+// Query rows handled by one prefill workgroup.
+constexpr int kFwdRowsPerTileBf16 = 256;
+constexpr int kFwdRowsPerTileF32 = 128;
+// The bf16 prefill kernel addresses rows inside a 64-key tile with 32-bit
+// byte offsets: key/value row strides (elements) are limited to 2^24.
+constexpr int64_t kFwdMaxKvRowStrideBf16 = int64_t(1) << 24;
 
 // One prefill launch: dense batched attention or packed variable-length
 // sequences.  All strides are in elements.

@@ -45,6 +45,14 @@ def test_exports_every_declared_function(L):
     assert {e for e in exported if e.startswith("fa_")} == set(names)
 
 
+def test_no_unresolved_library_symbols():
+    """Every kernel launch stub the library references is defined in it (a
+    missing stub only shows up when the library is loaded)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True)
+    own = [l for l in out.stdout.splitlines() if "_ZN2fa" in l or "device_stub" in l]
+    assert own == []
+
+
 def test_abi_version_and_strings(L):
     assert L.fa_abi_version() == 1
     for st in range(6):
@@ -110,6 +118,7 @@ def fwd_args(**kw):
     (dict(q=0x1002), fa.FA_ERR_BAD_SHAPE),
     (dict(k_stride=[1024, 129, 64]), fa.FA_ERR_BAD_SHAPE),
     (dict(v_stride=[1024, -128, 64]), fa.FA_ERR_BAD_SHAPE),
+    (dict(k_stride=[1 << 30, (1 << 24) + 8, 64]), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects_before_launch(L, kw, status):
     a = fwd_args(**kw)
@@ -149,6 +158,7 @@ def varlen_args(**kw):
     (dict(cu_seqlens=None), fa.FA_ERR_NULL_POINTER),
     (dict(q_stride=[100, 64]), fa.FA_ERR_BAD_SHAPE),
     (dict(o=0x1008), fa.FA_ERR_BAD_SHAPE),
+    (dict(v_stride=[(1 << 24) + 8, 64]), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_varlen_rejects_before_launch(L, kw, status):
     a = varlen_args(**kw)
