@@ -18,7 +18,9 @@
 //     (global_load_lds, 16 bytes per lane, no register staging) through a
 //     ring of 4 stages.  Rows are stored whole (d contiguous) with the 16-byte
 //     chunks of each row XOR-swizzled so that both the score-operand reads and
-//     the transposed value reads hit distinct banks.
+//     the transposed value reads hit distinct banks.  Only the waves in their
+//     softmax phase issue loads, spread over the softmax: a wave stalls while
+//     the CU's vector-memory path is busy, and the MFMA waves must not.
 //   * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16,
 //     so each lane's accumulator column is ONE query row: the row max and row
 //     sum are in-lane reductions plus one v_permlane32_swap, and the
@@ -28,16 +30,18 @@
 //     match), so P never leaves registers; the V^T operand is read from the
 //     row-major V tile with ds_read_b64_tr_b16 (a 4 x 16 transpose of 16-bit
 //     elements inside each 16-lane group).
-//   * ping-pong: each wave alternates an MFMA phase (P.V of the previous tile
-//     and the scores of the next) with a VALU phase (softmax).  Waves 4..7
+//   * ping-pong: each wave alternates an MFMA phase (the scores of the next
+//     tile and P.V of the previous one) with a VALU phase (softmax).  Waves 4..7
 //     run one phase behind waves 0..3 and every phase ends at a workgroup
 //     barrier, so on each SIMD one wave is in its MFMA phase while the other
 //     is in its softmax phase and both pipes stay busy.
 //   * scores are kept in base 2: x = s * scale * log2(e), p = 2^(x - m).
-//   * lazy correction: o and l are rescaled only when some row of the wave
-//     sees its max grow by more than 2^8; otherwise the weights are formed
-//     against the slightly stale reference (p <= 256).  Any reference gives
-//     the same o / l.
+//   * lazy correction: a tile's weights are formed against the reference
+//     max of an earlier tile, and the row max is not even taken, as long as
+//     no weight exceeds 2^16 (checked on each lane's partial sum).  Only
+//     then is the tile's max taken, o and l rescaled and the weights
+//     recomputed.  Any reference gives the same o / l; fp32 and bf16 carry
+//     weights up to 2^16 without loss of relative precision.
 //   * causal tiles above the diagonal are never visited; only tiles that
 //     straddle the diagonal or the sequence end are masked.
 //   * the first-tile NaN of "exp(-inf - -inf)" ("S12 FlashAttention", "Build
@@ -55,7 +59,15 @@ constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 static_assert(kBr == kFwdRowsPerTileBf16, "host tiling must match");
 constexpr int kBc = 64;            // keys per tile
 constexpr int kStages = 4;         // LDS ring depth
-constexpr float kLazyLog2 = 8.f;   // max growth (base 2) tolerated before correcting o and l
+#ifndef FA_K_AHEAD
+#define FA_K_AHEAD 4
+#endif
+#ifndef FA_V_AHEAD
+#define FA_V_AHEAD 4
+#endif
+constexpr int kKAhead = FA_K_AHEAD;  // score-operand reads issued ahead of their MFMA
+constexpr int kVAhead = FA_V_AHEAD;  // P.V MFMAs whose operand reads are issued ahead
+constexpr float kLazyBound = 65536.f;  // largest weight (2^16) formed against a stale reference
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -120,10 +132,10 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = kBc * D;            // elements per K or V tile
-  constexpr int RPI = 512 / D;             // rows per 1 KB DMA instruction
-  constexpr int IPW = kBc / RPI / kWaves;  // DMA instructions per wave per tile, per operand
-  constexpr int IPT = 2 * IPW;             // ... for K and V together
-  static_assert(IPW >= 1, "tile too small for the wave count");
+  constexpr int RPI = 512 / D;              // rows per 1 KB DMA instruction
+  constexpr int RPW = kBc / 4;              // rows per wave when one group loads an operand
+  constexpr int IPW = RPW / RPI;            // DMA instructions per wave per operand of a tile
+  static_assert(IPW >= 1 && IPW <= 4 && RPW % RPI == 0, "DMA split");
   __shared__ __attribute__((aligned(1024))) uint16_t k_s[kStages][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_s[kStages][TILE];
 
@@ -202,53 +214,54 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
   float m_run = -INFINITY;  // base-2 reference max of this lane's row
-  float l_run = 0.f;        // this half-wave's share of the running sum
+  float l_run = 0.f;        // this half-wave's share of the running sum (fp32 weights: LSE)
+  float lb_run = 0.f;       // ... of the bf16-rounded weights P.V uses (normalises o)
   const float c = p.scale_log2;
 
-  // DMA of one tile into its LDS stage; wave w covers rows 8w .. 8w+7.
-  // Lane l of instruction i writes the 16 bytes at LDS row (8w + i*RPI +
-  // l/CH), physical chunk l%CH, so it fetches the logical chunk the swizzle
-  // maps there.  The tile's base address is uniform (scalar registers); the
+  // DMA of one operand (K or V) of one tile into its LDS stage by the four
+  // waves of one group; wave w covers rows 16(w%4) .. 16(w%4)+15.  Lane l of
+  // instruction i writes the 16 bytes at LDS row (16(w%4) + i*RPI + l/CH),
+  // physical chunk l%CH, so it fetches the logical chunk the swizzle maps
+  // there.  The tile's base address is uniform (scalar registers); the
   // per-lane byte offsets within a tile are the same for every full tile
-  // (the host keeps them below 2^31).  In a tile that runs past the last key,
-  // rows past the end re-read the last key row: their weights are exactly
-  // zero and their values finite.
+  // (the host keeps them below 2^31).  In a tile that runs past the last
+  // key, rows past the end re-read the last key row: their weights are
+  // exactly zero and their values finite.
   const int drow = lane / CH;
   const int dpch = lane % CH;
+  const int wq = wave & 3;
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = wave * (kBc / kWaves) + i * RPI + drow;
+    const int r = wq * RPW + i * RPI + drow;
     koff[i] = (uint32_t)(((int64_t)r * p.k_ss + swz_k(CH, r, dpch) * 8) * 2);
     voff[i] = (uint32_t)(((int64_t)r * p.v_ss + swz_v(CH, r, dpch) * 8) * 2);
   }
-  auto dma = [&](int tile) {
+  // Instruction i of this wave's share of operand V_OP (K when false) of a tile.
+  auto dma_one = [&](int tile, bool v_op, int i) {
     const int st = tile % kStages;
-    const uint16_t* kt = kg + (int64_t)tile * kBc * p.k_ss;
-    const uint16_t* vt = vg + (int64_t)tile * kBc * p.v_ss;
+    const uint16_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
+    const int r0 = wq * RPW + i * RPI;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
     const int rows_left = nk - tile * kBc;  // uniform
-    if (rows_left >= kBc) {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int r0 = wave * (kBc / kWaves) + i * RPI;
-        dma_16b(kt, koff[i], __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&k_s[st][0] + r0 * D)));
-        dma_16b(vt, voff[i], __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&v_s[st][0] + r0 * D)));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < IPW; ++i) {
-        const int r0 = wave * (kBc / kWaves) + i * RPI;
-        const int r = r0 + drow;
-        const int rk = min(r, rows_left - 1);
-        const uint32_t ko = (uint32_t)(((int64_t)rk * p.k_ss + swz_k(CH, r, dpch) * 8) * 2);
-        const uint32_t vo = (uint32_t)(((int64_t)rk * p.v_ss + swz_v(CH, r, dpch) * 8) * 2);
-        dma_16b(kt, ko, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&k_s[st][0] + r0 * D)));
-        dma_16b(vt, vo, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&v_s[st][0] + r0 * D)));
-      }
+    uint32_t off = v_op ? voff[i] : koff[i];
+    if (rows_left < kBc) {
+      const int r = r0 + drow;
+      const int rk = min(r, rows_left - 1);
+      off = v_op ? (uint32_t)(((int64_t)rk * p.v_ss + swz_v(CH, r, dpch) * 8) * 2)
+                 : (uint32_t)(((int64_t)rk * p.k_ss + swz_k(CH, r, dpch) * 8) * 2);
     }
+    dma_16b(base, off, lds);
+  };
+  auto dma_op = [&](int tile, bool v_op) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i);
   };
 
-  if (nt > 0) dma(0);  // in flight while the Q fragments arrive
+  // Prologue loads: group 0 takes K, group 1 V.  Tile 0 flies while the Q
+  // fragments arrive.
+  if (nt > 0) dma_op(0, grp != 0);
 
   // Scores of one tile (S^T, two 32-key blocks).
   f32x16 sacc[2];
@@ -265,15 +278,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
         sacc[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], sacc[kb]);
       }
     }
-    // Keep four operand reads in flight ahead of the MFMAs (LDS latency is
-    // several MFMAs long).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // Keep kKAhead operand reads in flight ahead of the MFMAs (LDS latency
+    // is several MFMAs long).
+    __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
 #pragma unroll
-    for (int i = 0; i < D / 8 - 4; ++i) {
+    for (int i = 0; i < D / 8 - kKAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
   };
 
   // Softmax of tile t in place (scores -> weights), producing the bf16 B
@@ -283,7 +296,50 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // following P.V phase (o is not touched in between); l is corrected at once.
   bool corr = false;   // the reference moved in the last softmax: o must be scaled by alpha
   float alpha = 1.f;
-  auto softmax = [&](int t) {
+  // Weights p = 2^(s*c - m) of the tile for reference m: packed into the
+  // bf16 B operands pf of the P.V product.  Adds this lane's sums of the fp32
+  // weights to ps and of the bf16-rounded ones to pb (v_dot2 with (1, 1) on
+  // the packed pairs).  When dma_tile >= 0 the wave's share of operand
+  // DMA_V (K when false) of that tile is issued along the way, one
+  // instruction per chunk: the vector-memory path takes about 15-30 cycles
+  // per 1 KB instruction per CU and a wave stalls while it is busy, so the
+  // loads are spaced out and issued only by the group whose matrix pipe is
+  // idle.
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  auto weights = [&](float m, float& ps, float& pb, int dma_tile, bool dma_v) {
+    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    float pb2[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      if (dma_tile >= 0 && kc % (4 / IPW) == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_one(dma_tile, dma_v, kc / (4 / IPW));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int kb = kc >> 1;
+      const int r0 = 8 * (kc & 1);
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pv[j] = exp2_fast(__builtin_fmaf(sacc[kb][r0 + j], c, -m));
+        ps4[j & 3] += pv[j];
+      }
+      uint4 pw;
+      pw.x = pack_bf16x2(pv[0], pv[1]);
+      pw.y = pack_bf16x2(pv[2], pv[3]);
+      pw.z = pack_bf16x2(pv[4], pv[5]);
+      pw.w = pack_bf16x2(pv[6], pv[7]);
+      pb2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones2, pb2[0], false);
+      pb2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones2, pb2[1], false);
+      pb2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones2, pb2[0], false);
+      pb2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones2, pb2[1], false);
+      pf[kc] = __builtin_bit_cast(bf16x8, pw);
+    }
+    ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    pb = pb2[0] + pb2[1];
+  };
+
+  auto softmax = [&](int t, int dma_tile, bool dma_v) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
     if (need_mask) {
@@ -295,43 +351,33 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > kend) sacc[kb][r] = -INFINITY;
     }
-    float mx[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      mx[q] = fmaxf(sacc[q >> 1][8 * (q & 1)], sacc[q >> 1][8 * (q & 1) + 1]);
-#pragma unroll
-      for (int r = 2; r < 8; ++r) mx[q] = fmaxf(mx[q], sacc[q >> 1][8 * (q & 1) + r]);
-    }
-    const float tmax = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * c;
-    const float m_new = fmaxf(m_run, tmax);
-    corr = __any(m_new > m_run + kLazyLog2);
+    // Fast path: weights against the current reference m_run, without the
+    // tile's row max.  Every weight is at most this lane's partial sum, so a
+    // partial sum <= kLazyBound bounds them all; a larger, infinite or NaN
+    // sum (a large jump of the max, or no reference yet) sends the whole wave
+    // to the exact step, which takes the row max, moves the reference and
+    // recomputes the weights.
+    float ps, pb;
+    weights(m_run, ps, pb, dma_tile, dma_v);
+    corr = __any(!(ps <= kLazyBound));
     if (corr) {
+      float mx[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mx[q] = fmaxf(sacc[q >> 1][8 * (q & 1)], sacc[q >> 1][8 * (q & 1) + 1]);
+#pragma unroll
+        for (int r = 2; r < 8; ++r) mx[q] = fmaxf(mx[q], sacc[q >> 1][8 * (q & 1) + r]);
+      }
+      const float tmax = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * c;
+      const float m_new = fmaxf(m_run, tmax);
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
+      lb_run *= alpha;
       m_run = m_new;
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb, -1, false);
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = exp2_fast(__builtin_fmaf(sacc[kb][r], c, -m_use));
-        sacc[kb][r] = pv;
-        ps[r & 3] += pv;
-      }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int kb = kc >> 1;
-      const int r0 = 8 * (kc & 1);
-      uint4 pw;
-      pw.x = pack_bf16x2(sacc[kb][r0 + 0], sacc[kb][r0 + 1]);
-      pw.y = pack_bf16x2(sacc[kb][r0 + 2], sacc[kb][r0 + 3]);
-      pw.z = pack_bf16x2(sacc[kb][r0 + 4], sacc[kb][r0 + 5]);
-      pw.w = pack_bf16x2(sacc[kb][r0 + 6], sacc[kb][r0 + 7]);
-      pf[kc] = __builtin_bit_cast(bf16x8, pw);
-    }
+    l_run += ps;
+    lb_run += pb;
   };
 
   // O^T += V^T P^T over four 16-key chunks of tile t.  Contraction slot j of
@@ -368,13 +414,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
         oacc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[kc], oacc[db]);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // Two transposed reads per MFMA; kVAhead MFMAs' worth in flight.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
 #pragma unroll
-    for (int i = 0; i < D / 8 - 4; ++i) {
+    for (int i = 0; i < D / 8 - kVAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
   };
 
   // Phase schedule.  Global phases P = 0 .. 2*nt + 1, each ended by a
@@ -382,21 +429,24 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // tile t, then P.V of tile t - 1) in phase 2t and the softmax of tile t in
   // phase 2t + 1; group 1 runs the same sequence one phase later.  Scores go
   // first so that the next softmax waits only for them, not for the P.V
-  // products queued behind them on the matrix pipe.  Tile t is
-  // DMA'd at the start of phase 2t - 4 (prologue: tiles 0, 1) into stage
-  // t % 4, whose previous tile t - 4 was last read in phase 2t - 5; each wave
-  // waits for its share of tile (P+1)/2 at the end of odd phase P, just
-  // before group 0 first reads it.  The two groups' loops are written out
-  // separately so every phase is straight-line code.
-  auto phase_begin = [&](int P) {
-    if ((P & 1) == 0 && P / 2 + 2 < nt) dma(P / 2 + 2);
-  };
+  // products queued behind them on the matrix pipe.  So K of tile t is read
+  // in phases 2t and 2t + 1, V of tile t in phases 2t + 2 and 2t + 3.
+  //
+  // Loads come from the group in its softmax phase, one operand of one tile
+  // per phase, into stage t % 4: K of tile t in phase 2t - 4 by group 1 (K of
+  // tile t - 4 was last read in phase 2t - 7), V of tile t in phase 2t - 3 by
+  // group 0 (V of tile t - 4 was last read in phase 2t - 5).  The prologue
+  // loads tiles 0 and 1 (group 0 K, group 1 V).  At the end of odd phase P
+  // each wave waits for its share of tile (P+1)/2, which group 0 reads next;
+  // only its share of the following tile, issued later, may still be in
+  // flight.  The two groups' loops are written out separately so every phase
+  // is straight-line code.
   auto phase_end = [&](int P) {
     if (P & 1) {
       const int t_need = (P + 1) / 2;
       if (t_need < nt) {
         if (t_need + 1 < nt)
-          wait_vmcnt<IPT>();
+          wait_vmcnt<IPW>();
         else
           wait_vmcnt<0>();
       }
@@ -409,34 +459,27 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
     wait_vmcnt<0>();
-    if (nt > 1) dma(1);
+    if (nt > 1) dma_op(1, grp != 0);
     lds_barrier();
     if (grp == 0) {
-      phase_begin(0);
       scores(0);
       phase_end(0);
       for (int t = 0; t < nt; ++t) {
-        phase_begin(2 * t + 1);
-        softmax(t);
+        softmax(t, t + 2 < nt ? t + 2 : -1, true);
         phase_end(2 * t + 1);
-        phase_begin(2 * t + 2);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         phase_end(2 * t + 2);
       }
-      phase_begin(2 * nt + 1);
       phase_end(2 * nt + 1);
     } else {
-      phase_begin(0);
+      if (2 < nt) dma_op(2, false);
       phase_end(0);
-      phase_begin(1);
       scores(0);
       phase_end(1);
       for (int t = 0; t < nt; ++t) {
-        phase_begin(2 * t + 2);
-        softmax(t);
+        softmax(t, t + 3 < nt ? t + 3 : -1, false);
         phase_end(2 * t + 2);
-        phase_begin(2 * t + 3);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         phase_end(2 * t + 3);
@@ -446,8 +489,11 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 
   // Epilogue: O = o / l, LSE = (m + log2 l) * ln 2.
   const float l_tot = sum_halves(l_run);
+  const float lb_tot = sum_halves(lb_run);
   if (row < nq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // o / l with the sum of the weights the product actually used: the row
+    // is then a convex combination of value rows up to fp32 rounding.
+    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
     uint16_t* orow = (uint16_t*)p.o + o_base + (int64_t)row * p.o_ss;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
