@@ -51,35 +51,6 @@ float scale_log2(float scale) { return (float)((double)scale * 1.442695040888963
 constexpr int kDecodeBlock = 16;
 constexpr int kDecodeDim = 128;
 
-// Split size in tokens for the paged decode: explicit (num_splits > 0) or a
-// choice that gives every CU several workgroups without splitting finer
-// than needed.  Depends only on host-side sizes.
-int32_t decode_split_tokens(const fa_decode_paged_args* a) {
-  const int64_t maxlen = a->max_seq_len > 0 ? a->max_seq_len : 1;
-  int64_t splits;
-  if (a->num_splits > 0) {
-    splits = a->num_splits;
-  } else {
-    const int64_t pairs = (int64_t)a->batch * a->heads_kv;
-    const int64_t want = 4096;  // workgroups wanted in flight over 256 CUs
-    splits = pairs > 0 ? (want + pairs - 1) / pairs : 1;
-  }
-  int64_t st = (maxlen + splits - 1) / splits;
-  st = (st + kDecodeBlock - 1) / kDecodeBlock * kDecodeBlock;
-  if (a->num_splits <= 0) {
-    if (st > 1024) st = 1024;
-    if (st < 256) st = 256;
-  }
-  if (st < kDecodeBlock) st = kDecodeBlock;
-  return (int32_t)st;
-}
-
-int32_t decode_num_splits(const fa_decode_paged_args* a) {
-  const int64_t maxlen = a->max_seq_len > 0 ? a->max_seq_len : 1;
-  const int32_t st = decode_split_tokens(a);
-  return (int32_t)((maxlen + st - 1) / st);
-}
-
 fa_status check_decode(const fa_decode_paged_args* a) {
   if (!a) return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: args is NULL");
   if (a->batch < 0 || a->heads_q <= 0 || a->heads_kv <= 0 || a->max_seq_len < 0 ||
@@ -89,8 +60,9 @@ fa_status check_decode(const fa_decode_paged_args* a) {
     return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: heads_q (%d) is not a multiple of heads_kv (%d)",
                 a->heads_q, a->heads_kv);
   const int group = a->heads_q / a->heads_kv;
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: heads_q / heads_kv = %d, supported 1, 2, 4, 8", group);
+  if (group > fa::kDecodeMaxGroup)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: heads_q / heads_kv = %d, supported up to %d", group,
+                fa::kDecodeMaxGroup);
   if (a->head_dim != kDecodeDim)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d, supported 128", a->head_dim);
   if (a->block_size != kDecodeBlock)
@@ -99,12 +71,19 @@ fa_status check_decode(const fa_decode_paged_args* a) {
     return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: max_seq_len %d exceeds max_blocks_per_seq * block_size",
                 a->max_seq_len);
   if (a->batch > 65535) return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: batch %d > 65535", a->batch);
+  if ((int64_t)a->batch * ((a->max_seq_len + kDecodeBlock - 1) / kDecodeBlock) > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: batch * max_seq_len / block_size exceeds 2^31");
+  if (a->pool_stride[2] > fa::kDecodeMaxTokenStride)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: pool token stride above %lld elements",
+                (long long)fa::kDecodeMaxTokenStride);
+  if (a->num_splits > 65535)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: num_splits %d > 65535", a->num_splits);
   return FA_OK;
 }
 
-size_t decode_workspace(const fa_decode_paged_args* a) {
-  const size_t rows = (size_t)a->batch * a->heads_q * (size_t)decode_num_splits(a);
-  return rows * (kDecodeDim + 2) * sizeof(float);
+// Parts the key-block list is cut into; -1 if the device cannot be queried.
+int decode_parts(const fa_decode_paged_args* a) {
+  return fa::decode_num_parts(a->num_splits, a->batch, a->heads_q, a->heads_q / a->heads_kv, a->max_seq_len);
 }
 
 }  // namespace
@@ -229,12 +208,22 @@ FA_EXPORT fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
 
 FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) {
   if (check_decode(a) != FA_OK) return 0;
-  return decode_workspace(a);
+  const int parts = decode_parts(a);
+  if (parts < 1) {
+    fail(FA_ERR_HIP, "fa_decode_paged_workspace_size: cannot query the current device");
+    return 0;
+  }
+  return fa::decode_workspace_bytes(parts, a->batch, a->heads_q);
 }
 
 FA_EXPORT int32_t fa_decode_paged_num_splits(const fa_decode_paged_args* a) {
   if (check_decode(a) != FA_OK) return 0;
-  return decode_num_splits(a);
+  const int parts = decode_parts(a);
+  if (parts < 1) {
+    fail(FA_ERR_HIP, "fa_decode_paged_num_splits: cannot query the current device");
+    return 0;
+  }
+  return parts;
 }
 
 FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream) {
@@ -243,14 +232,18 @@ FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream)
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
     return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: scale must be positive and finite");
   if (a->batch == 0) return ok();
-  if (!a->q || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens || !a->o || !a->workspace)
-    return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: q, pools, block_table, seq_lens, o, workspace required");
+  if (!a->q || !a->seq_lens || !a->o || !a->workspace)
+    return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: q, seq_lens, o and workspace are required");
+  if (a->max_seq_len > 0 && (!a->k_pool || !a->v_pool || !a->block_table))
+    return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: pools and block_table are required when max_seq_len > 0");
   if (!strides_ok(a->pool_stride, 3, 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
     return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: strides must be non-negative multiples of 8 elements");
   if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->o) ||
       !aligned16(a->workspace))
     return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: q, pools, o and workspace must be 16-byte aligned");
-  const size_t need = decode_workspace(a);
+  const int parts = decode_parts(a);
+  if (parts < 1) return fail(FA_ERR_HIP, "fa_decode_paged: cannot query the current device");
+  const size_t need = fa::decode_workspace_bytes(parts, a->batch, a->heads_q);
   if (a->workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode_paged: workspace %zu bytes, need %zu", a->workspace_bytes,
                 need);
@@ -266,9 +259,8 @@ FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream)
   p.seq_lens = a->seq_lens;
   p.o = a->o;
   p.lse = a->lse;
-  p.num_splits = decode_num_splits(a);
-  p.split_tokens = decode_split_tokens(a);
-  const size_t rows = (size_t)a->batch * a->heads_q * (size_t)p.num_splits;
+  p.num_splits = parts;
+  const size_t rows = (size_t)a->heads_q * (size_t)(parts + a->batch);
   p.ws_o = (float*)a->workspace;
   p.ws_ml = p.ws_o + rows * kDecodeDim;
   p.batch = a->batch;

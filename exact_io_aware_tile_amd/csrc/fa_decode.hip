@@ -1,5 +1,5 @@
 // fa_decode.hip -- paged single-token decode with grouped-query heads, split
-// across workgroups (flash-decoding) and merged by a second kernel.
+// across waves (flash-decoding) and merged by a second kernel.
 //
 // Sources: "S12 FlashAttention" (llminference.xinbetween.com):
 //   * "What this unlocks beyond speed": tiles need not be contiguous -- each
@@ -10,22 +10,43 @@
 //     block table that loads the KV head shared by the query's group and
 //     updates (m, l, o);
 //   * "Build it / Implementation" (paged excerpt): block i holds
-//     min(block, seq_len - i*block) keys and the walk stops when that is <= 0.
+//     min(block, seq_len - i*block) keys and the walk stops when that is <= 0;
+//     the same section's remedy for exp(-inf - -inf): a finite initial max.
 // The merge of two partial states is the rule printed on the "FlashAttention"
 // page of tachyon.techntrek.in ("For engineers / Show the maths"):
 // m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2, and o rescales the same way.
 //
-// gfx950 mapping of the split kernel: one wave per (sequence, kv head, split),
-// no LDS and no barriers.  A 16-token x 128-dim bf16 block of one kv head is
-// 4 KB; every 16-byte load of the wave covers 8 token rows x 128 contiguous
-// bytes.  The G query heads of the group share every load (GQA).  q.k uses
-// v_dot2_f32_bf16 on the raw bf16 pairs, and a token's partial dot products
-// are summed across its 8 lanes with DPP moves.  Split boundaries are
-// multiples of the block size and depend only on logical token positions, and
-// nothing in the arithmetic depends on where a block sits in the pool, so a
-// permuted pool gives bit-identical results.
-#include <type_traits>
-
+// Work division (balanced split).  For one KV head, the key blocks of all
+// sequences, concatenated in batch order, form one list of U blocks.  It is
+// cut into P equal parts (P = num_splits, by default one per wave slot of
+// the device), one wave each, so every wave streams the same number of
+// blocks and all finish together whatever the mix of lengths.  A part may
+// end inside a sequence and may cover several short ones: it leaves one
+// partial state per (sequence, part) piece.  Piece (sequence b, part w) of
+// a query head is stored in that head's slot w + b -- unique, because
+// walking the pieces in order increases w, b or both -- so the workspace
+// holds P + batch slots per query head.  The cut depends only on logical
+// block positions: a permuted pool gives bit-identical results.
+//
+// Split kernel, gfx950 mapping: one wave per (part, kv head); all query
+// heads of the group (up to 16) ride in the 16 columns of the matrix
+// products, so every K/V byte is loaded once for the whole group.
+//   * scores S^T[16 tokens x 16 heads] = K Q^T on v_mfma_f32_16x16x32_bf16:
+//     lane l loads the A operand straight from the pool -- token l%16, dims
+//     32s + 8(l/16) .. +7 for s = 0..3 -- and holds Q of head l%16 as B;
+//   * the accumulator leaves lane l with tokens 4(l/16) .. +3 of head l%16,
+//     which is exactly the B operand layout of the second product
+//     O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k), so the weights never move
+//     between lanes; the lazy softmax per head runs on those 4 values;
+//   * V^T comes from a 4 KB LDS copy of the value block read with
+//     ds_read_b64_tr_b16 (four tokens of one dim per lane); the 16-byte
+//     chunks of each row are XOR-swizzled so the transposed reads of a
+//     half-wave hit distinct banks;
+//   * K and V of three blocks are in flight (a four-deep register ring)
+//     while one is consumed.
+// Lazy correction: weights are formed against the head's current reference
+// max until one would exceed 2^8; only then is the reference moved (the max
+// over the four lane groups holding that head) and (o, l) rescaled.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -34,284 +55,384 @@ namespace {
 
 constexpr int kBlock = 16;
 constexpr int kD = 128;
+constexpr float kLazyLog2 = 8.f;    // largest weight 2^8 against a stale reference
+constexpr float kInitMax = -1e30f;  // finite initial reference max
+constexpr int kMlStride = 4;        // workspace floats per partial: m, l, lb, unused
+constexpr int kSplitWavesPerCu = 8; // occupancy the split kernel is built for
 
-__device__ __forceinline__ void unpack8(const uint4 w, float (&f)[8]) {
-  f[0] = bf16_lo(w.x);
-  f[1] = bf16_hi(w.x);
-  f[2] = bf16_lo(w.y);
-  f[3] = bf16_hi(w.y);
-  f[4] = bf16_lo(w.z);
-  f[5] = bf16_hi(w.z);
-  f[6] = bf16_lo(w.w);
-  f[7] = bf16_hi(w.w);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
 }
 
-// Cross-lane moves inside a row of 16 lanes (DPP, no LDS traffic).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
 }
-constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowRor8 = 0x128;
 
-// Sum over the 8 lanes that share lane bits 3..5 (one token row of a block).
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp_mov<kQuadXor1>(x);
-  x += dpp_mov<kQuadXor2>(x);
-  x += dpp_mov<kRowHalfMirror>(x);  // lane i <-> 7 - i: the other quad of the 8
+__device__ __forceinline__ int clamp_len(int L, int maxlen) { return L < 0 ? 0 : (L > maxlen ? maxlen : L); }
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
   return x;
 }
 
-// 8 bf16 of a and b: acc + sum a_i * b_i (fp32 accumulation, v_dot2_f32_bf16).
-__device__ __forceinline__ float dot8(const uint4 a, const uint4 b, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
-  return acc;
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
 }
 
-// One block's K and V as this lane holds them: tokens t0 and t0 + 8, dims
-// 8c..8c+7 and 64+8c..64+8c+7.
-struct KV {
-  uint4 k[2][2];
-  uint4 v[2][2];
+// Key blocks of sequence b.
+__device__ __forceinline__ int seq_blocks(const DecodeParams& p, int b) {
+  return (clamp_len(p.seq_lens[b], p.max_seq_len) + kBlock - 1) / kBlock;
+}
+
+// U: key blocks of the whole batch (per kv head).
+__device__ int total_blocks(const DecodeParams& p, int lane) {
+  int s = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64)
+    if (c0 + lane < p.batch) s += seq_blocks(p, c0 + lane);
+  return __builtin_amdgcn_readfirstlane(wave_sum(s));
+}
+
+// The sequence b holding list position x (0 <= x < U) and the position of
+// b's first block.
+__device__ void locate(const DecodeParams& p, int lane, int x, int& b_out, int& first_out) {
+  int base = 0;
+  for (int c0 = 0; c0 < p.batch; c0 += 64) {
+    const int nb = c0 + lane < p.batch ? seq_blocks(p, c0 + lane) : 0;
+    const int incl = wave_incl_scan(nb, lane) + base;
+    const uint64_t hit = __ballot(incl > x);
+    if (hit) {
+      const int j = __builtin_ctzll(hit);
+      b_out = c0 + j;
+      first_out = __shfl(incl - nb, j, 64);
+      return;
+    }
+    base = __shfl(incl, 63, 64);
+  }
+  b_out = p.batch;
+  first_out = base;
+}
+
+// Position in a walk over the block list: sequence b, its block blk, its
+// block count nb and length L (all wave-uniform).
+struct Cursor {
+  int b, blk, nb, L;
 };
 
-// Split kernel.  Lane l = 8*t0 + c owns tokens t0 and t0 + 8 of every block
-// and the 16 dims {8c + e, 64 + 8c + e}; the 8 lanes of a token row read its
-// 256 bytes with two fully coalesced 128-byte runs.  Each lane runs the
-// recurrence on its own token stream (tokens t0, t0 + 8, t0 + 16, ...) with
-// its own (m, l, o) per query head -- the keys of the split are split once
-// more across the 8 token slots of the wave -- and the 8 slot states are
-// merged with the same rule at the end of the split.  Three K/V buffers keep
-// two blocks in flight while one is being consumed.
-template <int G>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+__device__ __forceinline__ void cursor_seq(const DecodeParams& p, Cursor& c, int b) {
+  c.b = b;
+  c.L = clamp_len(p.seq_lens[b], p.max_seq_len);
+  c.nb = (c.L + kBlock - 1) / kBlock;
+}
+
+// Next block; past a sequence's last block, the next sequence with keys.
+// Only called while blocks remain in the wave's part, so such a sequence exists.
+__device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
+  if (++c.blk < c.nb) return;
+  c.blk = 0;
+  do {
+    cursor_seq(p, c, c.b + 1);
+  } while (c.nb == 0);
+}
+
+// Physical 16-byte chunk of logical chunk c in value row r of the LDS copy.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 3) + 8 * ((r >> 2) & 1)); }
+
+// One block as this lane loads it: k[s] = token l%16, dims 32s + 8(l/16)
+// .. +7 (score A operand); v[s] = token 4s + l/16, dims 8(l%16) .. +7.
+struct Blk {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
+    const DecodeParams p) {
+  const int part = blockIdx.x;
+  const int g = blockIdx.y;  // kv head; query heads g*G .. g*G + G - 1
+  const int G = p.group;
   const int lane = threadIdx.x;
+  const int j = lane >> 4;   // lane group
+  const int n = lane & 15;   // token (K operand), head (scores), dim (V^T)
+  __shared__ __attribute__((aligned(16))) uint16_t v_s[kBlock * kD];
 
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-  const int t_begin = split * p.split_tokens;
-  if (t_begin >= L) return;  // no keys in this split; the combine skips it
-  const int t_end = L < t_begin + p.split_tokens ? L : t_begin + p.split_tokens;
-  const int blk0 = t_begin / kBlock;
-  const int blk1 = (t_end + kBlock - 1) / kBlock;
+  const int U = total_blocks(p, lane);
+  const int x0 = (int)((int64_t)part * U / p.num_splits);
+  const int x1 = (int)((int64_t)(part + 1) * U / p.num_splits);
+  if (x0 >= x1) return;
+  const int n_units = x1 - x0;
+  int b_first, first;
+  locate(p, lane, x0, b_first, first);
+  b_first = __builtin_amdgcn_readfirstlane(b_first);
+  first = __builtin_amdgcn_readfirstlane(first);
 
-  const int c = lane & 7;
-  const int t0 = lane >> 3;
+  Cursor ic, pc;  // issue and process positions
+  cursor_seq(p, ic, b_first);
+  ic.blk = x0 - first;
+  pc = ic;
 
-  uint4 qv[G][2];
+  // Loads address a block through a wave-uniform 64-bit base (scalar
+  // registers) plus a per-lane 32-bit byte offset that is the same for every
+  // block (the host keeps it below 2^31).
+  const char* __restrict__ kpool = (const char*)p.k_pool + (int64_t)g * p.p_hs * 2;
+  const char* __restrict__ vpool = (const char*)p.v_pool + (int64_t)g * p.p_hs * 2;
+  uint32_t koff[4], voff[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      qv[h][i] = *(const uint4*)((const uint16_t*)p.q + (int64_t)b * p.q_bs + (int64_t)(g * G + h) * p.q_hs +
-                                 64 * i + 8 * c);
-
-  float o[G][2][8];
-  float m[G], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][i][e] = 0.f;
+  for (int s = 0; s < 4; ++s) {
+    koff[s] = (uint32_t)((n * p.p_ts + 32 * s + 8 * j) * 2);
+    voff[s] = (uint32_t)(((4 * s + j) * p.p_ts + 8 * n) * 2);
   }
 
-  const uint16_t* __restrict__ kbase = (const uint16_t*)p.k_pool + (int64_t)g * p.p_hs + 8 * c;
-  const uint16_t* __restrict__ vbase = (const uint16_t*)p.v_pool + (int64_t)g * p.p_hs + 8 * c;
-  const int32_t* __restrict__ bt = p.block_table + (int64_t)b * p.max_blocks;
+  // Q of head n as the B operand of the score product (zero for columns
+  // past the group).
+  uint4 qf[4];
+  auto load_q = [&](int b) {
+    const uint16_t* qr = (const uint16_t*)p.q + (int64_t)b * p.q_bs + (int64_t)(g * G + n) * p.q_hs + 8 * j;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[s] = n < G ? *(const uint4*)(qr + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  load_q(pc.b);
+
+  f32x4 o[8];      // O^T: o[db][r] = dim 16db + 4j + r of head n
+  float m, l, lb;  // reference max (base 2), fp32 weight sum, bf16 weight sum
+  auto reset = [&]() {
+    m = kInitMax;
+    l = 0.f;
+    lb = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] = zero4();
+  };
+  reset();
+
+  int n_issued = 0;
+  auto issue = [&](Blk& B) {
+    if (n_issued < n_units) {
+      const int64_t base = (int64_t)p.block_table[(int64_t)ic.b * p.max_blocks + ic.blk] * p.p_bs * 2;
+      const char* kb = kpool + base;
+      const char* vb = vpool + base;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) B.k[s] = *(const uint4*)(kb + koff[s]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) B.v[s] = *(const uint4*)(vb + voff[s]);
+      if (++n_issued < n_units) cursor_next(p, ic);
+    }
+  };
+
+  const uint32_t ones2 = 0x3F803F80u;  // bf16 pair (1, 1)
   const float cs = p.scale_log2;
+  const int tk = n >> 2, tq = n & 3;
 
-  // Loads past the split's last block re-read that block (it is in cache);
-  // their tokens are masked when processed.
-  auto issue = [&](KV& B, int blk) {
-    const int bb = blk < blk1 ? blk : blk1 - 1;
-    const int64_t base = (int64_t)bt[bb] * p.p_bs;
+  // One block through the recurrence; tokens at or past VALID hold no key
+  // (only a sequence's last block has such tokens).
+  auto process = [&](const Blk& B, int valid) {
+    // Values to LDS (row = token, swizzled chunks).
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int s = 0; s < 4; ++s) {
+      const int r = 4 * s + j;
+      *(uint4*)&v_s[r * kD + swz(r, n) * 8] = B.v[s];
+    }
+    // Scores: sc[r] = S[token 4j + r][head n].
+    f32x4 sc = zero4();
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t off = base + (int64_t)(t0 + 8 * a) * p.p_ts + 64 * i;
-        B.k[a][i] = *(const uint4*)(kbase + off);
-        B.v[a][i] = *(const uint4*)(vbase + off);
+    for (int s = 0; s < 4; ++s)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, B.k[s]),
+                                                  __builtin_bit_cast(bf16x8, qf[s]), sc, 0, 0, 0);
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = 4 * j + r < valid ? sc[r] * cs : -INFINITY;
+    const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__any(xm > m + kLazyLog2)) {
+      float mx = fmaxf(xm, __shfl_xor(xm, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float al = exp2_fast(m - mn);
+      m = mn;
+      l *= al;
+      lb *= al;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[db][r] *= al;
+    }
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = exp2_fast(x[r] - m);
+    l += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    const uint32_t p01 = pack_bf16x2(pw[0], pw[1]);
+    const uint32_t p23 = pack_bf16x2(pw[2], pw[3]);
+    lb = dot2(p01, ones2, lb);
+    lb = dot2(p23, ones2, lb);
+    const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+    // Value tokens past the end may hold anything: clear them so that a
+    // zero weight cannot meet a NaN.
+    uint32_t keep0 = 0xFFFFFFFFu, keep1 = 0xFFFFFFFFu;
+    if (valid < kBlock) {
+      keep0 = (4 * j + 0 < valid ? 0x0000FFFFu : 0u) | (4 * j + 1 < valid ? 0xFFFF0000u : 0u);
+      keep1 = (4 * j + 2 < valid ? 0x0000FFFFu : 0u) | (4 * j + 3 < valid ? 0xFFFF0000u : 0u);
+    }
+    // O^T += V^T P^T per 16-dim block: lane 4k+q of group j reads token
+    // 4j + k, dims 16db + 4q .. +3; the transposed read leaves lane n with
+    // dim 16db + n of tokens 4j .. 4j+3.
+    const int vr = 4 * j + tk;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)&v_s[vr * kD + swz(vr, 2 * db + (tq >> 1)) * 8 + 4 * (tq & 1)]);
+      uint2 w = __builtin_bit_cast(uint2, vt);
+      w.x &= keep0;
+      w.y &= keep1;
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, w), pb, o[db], 0, 0, 0);
+    }
+  };
+
+  // End of a piece: sum the four lane groups' weight sums and store the
+  // piece's partial state for the group's heads in slot part + b.
+  const int S = p.num_splits + p.batch;
+  auto flush = [&](int b) {
+    float lt = l + __shfl_xor(l, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    float lbt = lb + __shfl_xor(lb, 16, 64);
+    lbt += __shfl_xor(lbt, 32, 64);
+    if (n < G) {
+      const int64_t row = (int64_t)(g * G + n) * S + part + b;
+      float* dst = p.ws_o + row * kD + 4 * j;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
+      if (j == 0) *(float4*)(p.ws_ml + row * kMlStride) = make_float4(m, lt, lbt, 0.f);
+    }
+  };
+
+  int n_done = 0;
+  auto step = [&](const Blk& B) {
+    if (n_done >= n_units) return;
+    const bool last_blk = pc.blk == pc.nb - 1;
+    process(B, last_blk ? pc.L - pc.blk * kBlock : kBlock);
+    ++n_done;
+    if (last_blk || n_done == n_units) {
+      flush(pc.b);
+      if (n_done < n_units) {
+        reset();
+        cursor_next(p, pc);
+        load_q(pc.b);
       }
-  };
-
-  // One block through the recurrence.  TAIL masks tokens at or past t_end
-  // (only the sequence's last block can hold such tokens).
-  auto process = [&](const KV& B, int blk, auto tail) {
-    constexpr bool TAIL = decltype(tail)::value;
-    const int tok0 = blk * kBlock;
-    const bool ok0 = !TAIL || tok0 + t0 < t_end;
-    const bool ok1 = !TAIL || tok0 + t0 + 8 < t_end;
-    float s[2][G];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[a][h] = sum8(dot8(qv[h][1], B.k[a][1], dot8(qv[h][0], B.k[a][0], 0.f)));
-    float v0[2][8], v1[2][8];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      unpack8(B.v[0][i], v0[i]);
-      unpack8(B.v[1][i], v1[i]);
-      if (TAIL) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v0[i][e] = ok0 ? v0[i][e] : 0.f;
-          v1[i][e] = ok1 ? v1[i][e] : 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float x0 = ok0 ? s[0][h] : -INFINITY;
-      const float x1 = ok1 ? s[1][h] : -INFINITY;
-      const float m_new = fmaxf(m[h], fmaxf(x0, x1) * cs);
-      const float mu = (!TAIL || m_new != -INFINITY) ? m_new : 0.f;
-      const float alpha = exp2_fast(m[h] - mu);
-      const float p0 = exp2_fast(__builtin_fmaf(x0, cs, -mu));
-      const float p1 = exp2_fast(__builtin_fmaf(x1, cs, -mu));
-      l[h] = __builtin_fmaf(alpha, l[h], p0 + p1);
-      m[h] = m_new;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          o[h][i][e] = __builtin_fmaf(p1, v1[i][e], __builtin_fmaf(p0, v0[i][e], o[h][i][e] * alpha));
-    }
-  };
-  // Blocks wholly inside the split take the unmasked path; blocks past the
-  // split's end (the ring's overrun) are skipped.  The branch is uniform.
-  auto step = [&](const KV& B, int blk) {
-    if (blk * kBlock + kBlock <= t_end) {
-      process(B, blk, std::false_type{});
-    } else if (blk < blk1) {
-      process(B, blk, std::true_type{});
+    } else {
+      ++pc.blk;
     }
   };
 
-  // The scheduling barriers keep each ring refill where it is written, two
+  // The scheduling barriers keep each ring refill where it is written, three
   // blocks ahead of its use, instead of letting the scheduler sink the loads
   // next to their consumers.
-  KV A, B, C;
-  issue(A, blk0);
-  issue(B, blk0 + 1);
-  issue(C, blk0 + 2);
+  Blk A, B, C, D;
+  issue(A);
+  issue(B);
+  issue(C);
+  issue(D);
   __builtin_amdgcn_sched_barrier(0);
-  for (int blk = blk0; blk < blk1; blk += 3) {
-    step(A, blk);
+  for (int u = 0; u < n_units; u += 4) {
+    step(A);
     __builtin_amdgcn_sched_barrier(0);
-    issue(A, blk + 3);
+    issue(A);
     __builtin_amdgcn_sched_barrier(0);
-    step(B, blk + 1);
+    step(B);
     __builtin_amdgcn_sched_barrier(0);
-    issue(B, blk + 4);
+    issue(B);
     __builtin_amdgcn_sched_barrier(0);
-    step(C, blk + 2);
+    step(C);
     __builtin_amdgcn_sched_barrier(0);
-    issue(C, blk + 5);
+    issue(C);
     __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // Merge the 8 token-slot states (lane bits 3..5) pairwise.
-#pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    const int mask = 8 << st;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = st == 0 ? dpp_mov<kRowRor8>(m[h]) : __shfl_xor(m[h], mask, 64);
-      const float lo = st == 0 ? dpp_mov<kRowRor8>(l[h]) : __shfl_xor(l[h], mask, 64);
-      const float M = fmaxf(m[h], mo);
-      const float mu = M == -INFINITY ? 0.f : M;
-      const float w = exp2_fast(m[h] - mu);
-      const float wo = exp2_fast(mo - mu);
-      l[h] = w * l[h] + wo * lo;
-      m[h] = M;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float oo = st == 0 ? dpp_mov<kRowRor8>(o[h][i][e]) : __shfl_xor(o[h][i][e], mask, 64);
-          o[h][i][e] = w * o[h][i][e] + wo * oo;
-        }
-    }
-  }
-
-  if (t0 == 0) {
-    const int64_t row0 = ((int64_t)b * p.heads_q + (int64_t)g * G) * p.num_splits + split;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* dst = p.ws_o + (row0 + (int64_t)h * p.num_splits) * kD + 8 * c;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        *(float4*)(dst + 64 * i) = make_float4(o[h][i][0], o[h][i][1], o[h][i][2], o[h][i][3]);
-        *(float4*)(dst + 64 * i + 4) = make_float4(o[h][i][4], o[h][i][5], o[h][i][6], o[h][i][7]);
-      }
-      if (c == 0) {
-        float* ml = p.ws_ml + (row0 + (int64_t)h * p.num_splits) * 2;
-        ml[0] = m[h];
-        ml[1] = l[h];
-      }
-    }
+    step(D);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(D);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One wave per (sequence, query head): merge the sequence's non-empty splits.
+// One wave per (sequence, query head): merge the partial states of the
+// sequence's pieces.  Pieces of sequence b are those of the parts holding
+// its first and last blocks and every non-empty part between; part w holds
+// list positions [w*U/P, (w+1)*U/P), so position x lies in part
+// ceil((x+1)*P/U) - 1.
 __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-  const int ns = (L + p.split_tokens - 1) / p.split_tokens;
-  const int64_t row0 = ((int64_t)b * p.heads_q + h) * p.num_splits;
-  const float* ml = p.ws_ml + row0 * 2;
+  const int U = total_blocks(p, lane);
+  // first block position of sequence b, and its block count
+  int first = 0;
+  for (int c0 = 0; c0 < b; c0 += 64)
+    if (c0 + lane < b) first += seq_blocks(p, c0 + lane);
+  first = __builtin_amdgcn_readfirstlane(wave_sum(first));
+  const int nb = seq_blocks(p, b);
 
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  const float m_use = M == -INFINITY ? 0.f : M;
-  float l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2_fast(ml[2 * s] - m_use);
-    l = __builtin_fmaf(w, ml[2 * s + 1], l);
-    const float2 v = *(const float2*)(p.ws_o + (row0 + s) * kD + 2 * lane);
-    o0 = __builtin_fmaf(w, v.x, o0);
-    o1 = __builtin_fmaf(w, v.y, o1);
+  const int P = p.num_splits;
+  const int S = P + p.batch;
+  float M = -INFINITY, l = 0.f, lb = 0.f, o0 = 0.f, o1 = 0.f;
+  if (nb > 0) {
+    const int w0 = (int)(((int64_t)(first + 1) * P + U - 1) / U) - 1;
+    const int w1 = (int)(((int64_t)(first + nb) * P + U - 1) / U) - 1;
+    const int64_t row0 = (int64_t)h * S + b;
+    // Parts with an empty range (possible when U < P) hold no piece.
+    auto empty = [&](int w) { return (int64_t)w * U / P == (int64_t)(w + 1) * U / P; };
+    for (int w = w0; w <= w1; ++w)
+      if (!empty(w)) M = fmaxf(M, p.ws_ml[(row0 + w) * kMlStride]);
+    for (int w = w0; w <= w1; ++w) {
+      if (empty(w)) continue;
+      const float4 ml = *(const float4*)(p.ws_ml + (row0 + w) * kMlStride);
+      const float wt = exp2_fast(ml.x - M);
+      l = __builtin_fmaf(wt, ml.y, l);
+      lb = __builtin_fmaf(wt, ml.z, lb);
+      const float2 v = *(const float2*)(p.ws_o + (row0 + w) * kD + 2 * lane);
+      o0 = __builtin_fmaf(wt, v.x, o0);
+      o1 = __builtin_fmaf(wt, v.y, o1);
+    }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  // o / lb: the weights P.V used, so the row is a convex combination of
+  // value rows up to fp32 rounding; LSE from the fp32 weights.
+  const float inv = lb > 0.f ? 1.f / lb : 0.f;
   uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.o_bs + (int64_t)h * p.o_hs;
   *(uint32_t*)(orow + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
   if (p.lse && lane == 0)
     p.lse[(int64_t)b * p.heads_q + h] = l > 0.f ? (M + log2_fast(l)) * kLn2 : -INFINITY;
 }
 
-template <int G>
-hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(p.num_splits, p.heads_kv, p.batch), dim3(64), 0,
-                     stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace
 
+int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len) {
+  if (num_splits > 0) return num_splits;
+  // One part per wave slot of the device (the split kernel is built for two
+  // waves per SIMD, eight per CU), spread over the kv heads; no more parts
+  // than about one per 4 blocks of the largest possible batch.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int64_t heads_kv = group > 0 ? heads_q / group : 1;
+  int64_t parts = (int64_t)cus * kSplitWavesPerCu / (heads_kv > 0 ? heads_kv : 1);
+  const int64_t max_units = (int64_t)batch * ((max_seq_len + kBlock - 1) / kBlock);
+  if (parts > (max_units + 3) / 4) parts = (max_units + 3) / 4;
+  if (parts < 1) parts = 1;
+  return (int)parts;
+}
+
+size_t decode_workspace_bytes(int parts, int batch, int heads_q) {
+  const size_t rows = (size_t)heads_q * (size_t)(parts + batch);
+  return rows * (kD + kMlStride) * sizeof(float);
+}
+
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  hipError_t e;
-  switch (p.group) {
-    case 1: e = launch_split<1>(p, stream); break;
-    case 2: e = launch_split<2>(p, stream); break;
-    case 4: e = launch_split<4>(p, stream); break;
-    case 8: e = launch_split<8>(p, stream); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL(decode_split_kernel, dim3(p.num_splits, p.heads_kv), dim3(64), 0, stream, p);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(p.heads_q, p.batch), dim3(64), 0, stream, p);
   return hipGetLastError();

@@ -38,6 +38,12 @@ struct FwdParams {
   float scale_log2;      // scale * log2(e): scores are kept in base 2
 };
 
+// Paged decode: query heads per kv head (one wave serves the whole group),
+// and the largest pool token stride (elements) the kernel's 32-bit per-lane
+// offsets inside a block can address.
+constexpr int kDecodeMaxGroup = 16;
+constexpr int64_t kDecodeMaxTokenStride = int64_t(1) << 26;
+
 // Paged decode: split kernel followed by the combine kernel.
 struct DecodeParams {
   const void* q;
@@ -50,16 +56,19 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* o;
   float* lse;
-  float* ws_o;   // [batch, heads_q, num_splits, head_dim] fp32 partial o
-  float* ws_ml;  // [batch, heads_q, num_splits, 2] fp32 partial (m, l), m in base 2
+  float* ws_o;   // [heads_q, num_splits + batch, head_dim] fp32 partial o
+  float* ws_ml;  // [heads_q, num_splits + batch, 4] fp32 partial (m, l, lb, -), m in base 2
   int32_t batch, heads_q, heads_kv, group, max_blocks, max_seq_len;
-  int32_t num_splits;       // grid extent in splits
-  int32_t split_tokens;     // tokens per split, a multiple of the block size
+  int32_t num_splits;  // parts the block list of one kv head is cut into
   float scale_log2;
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+// Parts for a requested num_splits (0: one per wave slot of the current
+// device, or of a 256-CU device when none can be queried).
+int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len);
+size_t decode_workspace_bytes(int parts, int batch, int heads_q);
 
 }  // namespace fa

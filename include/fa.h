@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -131,14 +131,19 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
 
 /*
  * fa_decode_paged -- one query token per sequence over a paged KV pool
- * (flash-decoding: the keys of each sequence are split across workgroups
- * and the partial (m, l, o) states are merged by a second kernel).
+ * (flash-decoding: the keys are split across waves and the partial
+ * (m, l, o) states are merged by a second kernel).
+ * "S12 FlashAttention" (llminference.xinbetween.com): "What this unlocks
+ * beyond speed" (tiles fetched through a block table; keys split across
+ * thread blocks, partial states combined), "How this composes with what
+ * you already built" (one loop with the block-table indirection and the
+ * group's shared KV head), "Build it / Implementation" (the paged loop).
  *
  *   q   [batch, heads_q, head_dim] bf16, strides q_stride = {batch, head}
  *   k_pool, v_pool: bf16 block pools addressed with element strides
  *       pool_stride = {block, head, token}; the default layout is
  *       [num_blocks, heads_kv, block_size, head_dim].  Both pools share the
- *       strides.
+ *       strides; the token stride is at most 2^26 elements.
  *   block_table: DEVICE int32 [batch, max_blocks_per_seq] (row stride
  *       max_blocks_per_seq); logical key t of sequence b lives in block
  *       block_table[b][t / block_size], slot t % block_size.  Entries past
@@ -146,16 +151,22 @@ fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
  *       must lie in [0, num_blocks): the kernel does not check them.
  *   seq_lens: DEVICE int32 [batch], each in [0, max_seq_len].
  *   o   [batch, heads_q, head_dim] bf16, strides o_stride (written)
- *   lse [batch, heads_q] fp32 contiguous (written; may be NULL)
- *   max_seq_len: HOST-side upper bound on seq_lens (sizes the split grid),
- *       at most max_blocks_per_seq * block_size.
- *   num_splits: maximum number of key splits per sequence, 0 = library
- *       choice.  Split boundaries depend only on logical token positions,
- *       so a permuted pool gives bit-identical results.
+ *   lse [batch, heads_q] fp32 contiguous (written; may be NULL).  A sequence
+ *       with no keys gets o = 0 and lse = -inf.
+ *   max_seq_len: HOST-side upper bound on seq_lens, at most
+ *       max_blocks_per_seq * block_size; batch * ceil(max_seq_len /
+ *       block_size) must stay below 2^31.
+ *   num_splits: the key blocks of all sequences of one KV head, taken in
+ *       batch order, are cut into num_splits equal parts, one wave each
+ *       (0 = library choice: one part per wave slot of the device, at most
+ *       about one per four blocks).  The cut depends only on logical
+ *       positions, so a permuted pool gives bit-identical results.
  *   workspace: DEVICE scratch of at least fa_decode_paged_workspace_size()
- *       bytes, owned by the caller; contents on entry are ignored.
+ *       bytes, owned by the caller, 16-byte aligned; contents on entry are
+ *       ignored.  Holds heads_q * (parts + batch) partial states of
+ *       head_dim + 4 floats.
  *
- * Supported: bf16, head_dim 128, block_size 16, heads_q / heads_kv <= 8.
+ * Supported: bf16, head_dim 128, block_size 16, heads_q / heads_kv <= 16.
  */
 typedef struct {
   const void *q;
@@ -175,13 +186,14 @@ typedef struct {
 } fa_decode_paged_args;
 
 /* Bytes of workspace fa_decode_paged needs for these arguments (0 on invalid
- * arguments).  Depends only on batch, heads_q, head_dim, max_seq_len,
- * block_size and num_splits. */
+ * arguments).  Depends on batch, heads_q, heads_kv, max_seq_len, num_splits
+ * and, when num_splits is 0, the current device's compute-unit count. */
 size_t fa_decode_paged_workspace_size(const fa_decode_paged_args *args);
 
 fa_status fa_decode_paged(const fa_decode_paged_args *args, void *stream);
 
-/* The number of key splits fa_decode_paged will use for these arguments. */
+/* The number of parts fa_decode_paged will cut each KV head's key blocks
+ * into for these arguments (0 on invalid arguments). */
 int32_t fa_decode_paged_num_splits(const fa_decode_paged_args *args);
 
 /* Static text for a status code. */

@@ -54,7 +54,9 @@ def test_no_unresolved_library_symbols():
 
 
 def test_abi_version_and_strings(L):
-    assert L.fa_abi_version() == 1
+    with open(os.path.join(ROOT, "include", "fa.h")) as f:
+        declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
+    assert L.fa_abi_version() == declared == 2
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -192,8 +194,8 @@ def decode_args(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(heads_q=30), fa.FA_ERR_BAD_SHAPE),
-    (dict(heads_q=24), fa.FA_ERR_UNSUPPORTED),   # group 3
-    (dict(heads_kv=2), fa.FA_ERR_UNSUPPORTED),   # group 16
+    (dict(heads_kv=1), fa.FA_ERR_UNSUPPORTED),   # group 32 > 16
+    (dict(pool_stride=[8 * 16 * 128, 16 * 128, (1 << 26) + 8]), fa.FA_ERR_UNSUPPORTED),
     (dict(head_dim=64), fa.FA_ERR_UNSUPPORTED),
     (dict(block_size=32), fa.FA_ERR_UNSUPPORTED),
     (dict(max_seq_len=64 * 16 + 1), fa.FA_ERR_BAD_SHAPE),
@@ -212,17 +214,24 @@ def test_decode_rejects_before_launch(L, kw, status):
 
 
 def test_decode_sizes(L):
+    # Explicit num_splits: that many parts of the concatenated block list per
+    # kv head; the workspace holds (parts + batch) slots of 128 + 4 floats
+    # per query head.
     a = decode_args(num_splits=4)
+    assert L.fa_decode_paged_num_splits(ctypes.byref(a)) == 4
+    assert L.fa_decode_paged_workspace_size(ctypes.byref(a)) == 32 * (4 + 4) * (128 + 4) * 4
+    a = decode_args(num_splits=7)
+    assert L.fa_decode_paged_num_splits(ctypes.byref(a)) == 7
+    # Automatic: one part per wave slot (8 per CU) spread over the 8 kv
+    # heads, at most about one part per 4 blocks of the largest batch
+    # (4 sequences x ceil(1000 / 16) = 252 blocks -> 63).
+    a = decode_args()
     ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
-    assert ns == 4  # 1000 tokens in splits of 256
-    assert L.fa_decode_paged_workspace_size(ctypes.byref(a)) == 4 * 32 * 4 * (128 + 2) * 4
-    a = decode_args(num_splits=7, max_seq_len=1000)
+    assert ns == 63
+    assert L.fa_decode_paged_workspace_size(ctypes.byref(a)) == 32 * (63 + 4) * (128 + 4) * 4
+    a = decode_args(max_seq_len=64 * 16, max_blocks_per_seq=64, batch=64)
     ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
-    st = -(-(-(-1000 // 7)) // 16) * 16  # ceil(1000/7) rounded up to 16 = 144
-    assert ns == -(-1000 // st)
-    a = decode_args()  # auto: splits of 256..1024 tokens
-    ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
-    assert 1 <= ns <= -(-1000 // 256)
+    assert 1 <= ns <= 64 * 64 // 4
     bad = decode_args(head_dim=64)
     assert L.fa_decode_paged_workspace_size(ctypes.byref(bad)) == 0
     assert L.fa_decode_paged_num_splits(ctypes.byref(bad)) == 0

@@ -278,9 +278,11 @@ def decode_gpu(fa, case, num_splits=0, k_pool=None, v_pool=None, table=None):
     return o, lse
 
 
-@pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("num_splits", [0, 1, 3])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 50])
 def test_decode_parity(gpu, group, num_splits):
+    # lengths: one token, a full block, a block and one token, a zero-length
+    # sequence in the middle, tails of every residue class mod 16
     lens = [1, 16, 17, 100, 0, 333, 48, 1000]
     hkv = 2
     case = inputs.paged_case(300 + group, lens, hkv * group, hkv, 128, pad_blocks=2)
@@ -289,6 +291,17 @@ def test_decode_parity(gpu, group, num_splits):
                                          case["seq_lens"])
     check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
           f"decode group={group} splits={num_splits}")
+
+
+@pytest.mark.parametrize("lens", [[0, 0, 5], [5, 0, 0], [0], [16, 0, 16, 0, 1]])
+def test_decode_empty_sequences(gpu, lens):
+    case = inputs.paged_case(330 + len(lens), lens, 8, 2, 128, pad_blocks=1)
+    for ns in (0, 2, 9):
+        o, lse = decode_gpu(gpu, case, num_splits=ns)
+        o_ref, lse_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                             case["seq_lens"])
+        check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+              f"decode lens={lens} splits={ns}")
 
 
 def test_decode_paged_equals_contiguous_bitwise(gpu):
