@@ -146,15 +146,24 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Work item.  Workgroups are dealt round-robin to the 8 XCDs; renumber so
-  // each XCD receives a contiguous run of (sequence, head) pairs (their K/V
-  // stay in that XCD's L2), and within a pair the heaviest causal query
-  // tiles (the last ones) come first.
+  // Work item.  Workgroups are dealt round-robin to the 8 XCDs and each
+  // XCD starts them in order as its CUs free up.  When the (sequence, head)
+  // pairs split evenly, XCD x takes a contiguous run of pairs (their K/V stay
+  // in its L2) and starts its items longest first: all pairs' last query
+  // tiles (the heaviest under a causal mask), then the ones before, ...
   const int nwg = gridDim.x;
   const int w = blockIdx.x;
-  const int lin = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const int qt = p.num_qtiles - 1 - (lin % p.num_qtiles);
-  const int bh = lin / p.num_qtiles;
+  const int npairs = nwg / p.num_qtiles;
+  int qt, bh;
+  if (npairs % 8 == 0) {
+    const int px = npairs / 8;  // pairs per XCD
+    const int j = w / 8;        // rank of this workgroup on its XCD
+    qt = p.num_qtiles - 1 - j / px;
+    bh = (w % 8) * px + j % px;
+  } else {
+    qt = p.num_qtiles - 1 - (w % p.num_qtiles);
+    bh = w / p.num_qtiles;
+  }
   const int h = bh % p.heads_q;
   const int b = bh / p.heads_q;
 
@@ -487,27 +496,38 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     }
   }
 
-  // Epilogue: O = o / l, LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = o / l, LSE = (m + log2 l) * ln 2.  o / l uses the sum of
+  // the weights the product actually used, so each row is a convex
+  // combination of value rows up to fp32 rounding.
   const float l_tot = sum_halves(l_run);
   const float lb_tot = sum_halves(lb_run);
-  if (row < nq) {
-    // o / l with the sum of the weights the product actually used: the row
-    // is then a convex combination of value rows up to fp32 rounding.
-    const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
-    uint16_t* orow = (uint16_t*)p.o + o_base + (int64_t)row * p.o_ss;
+  const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+  // The wave's 32 output rows go through LDS (the tile ring is idle: every
+  // tile has been consumed behind the last barrier) so that global stores
+  // write whole rows, 16 bytes per lane, instead of 8-byte pieces of 64
+  // rows.  Staging rows are 16-byte-chunk swizzled like the key tiles.
+  uint16_t* stage = &k_s[0][0] + wave * (32 * D);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = db * 32 + 8 * gq + 4 * hi;
-        uint2 st;
-        st.x = pack_bf16x2(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv);
-        st.y = pack_bf16x2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
-        *(uint2*)(orow + d) = st;
-      }
-    if (p.lse && hi == 0)
-      p.lse[lse_base + row] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
+    for (int gq = 0; gq < 4; ++gq) {
+      uint2 st;
+      st.x = pack_bf16x2(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv);
+      st.y = pack_bf16x2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv);
+      *(uint2*)&stage[l32 * D + ((4 * db + gq) ^ (l32 & (CH - 1))) * 8 + 4 * hi] = st;
+    }
+  constexpr int RPS = 64 / CH;  // rows per store instruction
+  uint16_t* __restrict__ og = (uint16_t*)p.o + o_base;
+#pragma unroll
+  for (int s = 0; s < 32 / RPS; ++s) {
+    const int r = s * RPS + lane / CH;
+    const int cc = lane % CH;
+    const uint4 v = *(const uint4*)&stage[r * D + (cc ^ (r & (CH - 1))) * 8];
+    const int orow = q0 + 8 * r + wave;
+    if (orow < nq) *(uint4*)(og + (int64_t)orow * p.o_ss + cc * 8) = v;
   }
+  if (row < nq && p.lse && hi == 0)
+    p.lse[lse_base + row] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
