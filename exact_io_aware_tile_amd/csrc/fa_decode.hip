@@ -43,7 +43,7 @@
 //     chunks of each row are XOR-swizzled so the transposed reads of a
 //     half-wave hit distinct banks;
 //   * K and V of three blocks are in flight (a four-deep register ring)
-//     while one is consumed.
+//     while one is consumed; the pool is read with non-temporal loads.
 // Lazy correction: weights are formed against the head's current reference
 // max until one would exceed 2^8; only then is the reference moved (the max
 // over the four lane groups holding that head) and (o, l) rescaled.
@@ -145,6 +145,14 @@ __device__ __forceinline__ void cursor_next(const DecodeParams& p, Cursor& c) {
   } while (c.nb == 0);
 }
 
+// 16 bytes of the KV pool, read once: a non-temporal load (streams past the
+// caches instead of displacing lines that are reused).
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Physical 16-byte chunk of logical chunk c in value row r of the LDS copy.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 3) + 8 * ((r >> 2) & 1)); }
 
@@ -220,9 +228,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       const char* kb = kpool + base;
       const char* vb = vpool + base;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) B.k[s] = *(const uint4*)(kb + koff[s]);
+      for (int s = 0; s < 4; ++s) B.k[s] = load_stream(kb + koff[s]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) B.v[s] = *(const uint4*)(vb + voff[s]);
+      for (int s = 0; s < 4; ++s) B.v[s] = load_stream(vb + voff[s]);
       if (++n_issued < n_units) cursor_next(p, ic);
     }
   };
