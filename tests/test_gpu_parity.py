@@ -200,7 +200,9 @@ def test_prefill_full_size_properties(gpu):
     vf = v.float()
     vmin = torch.cummin(vf, dim=1).values  # causal: keys 0..i
     vmax = torch.cummax(vf, dim=1).values
-    slack = 1e-2
+    # The exact row lies in the hull; the bf16 contract allows max |dO| of
+    # TOL["bf16"][0], so the GPU row lies within the hull widened by that.
+    slack = TOL["bf16"][0]
     assert bool((of >= vmin - slack).all()) and bool((of <= vmax + slack).all())
     # LSE >= the row's own diagonal score (that key is always visible)
     diag = (q.float() * k.float()).sum(-1) / math.sqrt(case["d"])  # [B, N, H]
