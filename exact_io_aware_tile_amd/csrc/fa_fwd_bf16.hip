@@ -34,7 +34,8 @@
 //     tile and P.V of the previous one) with a VALU phase (softmax).  Waves 4..7
 //     run one phase behind waves 0..3 and every phase ends at a workgroup
 //     barrier, so on each SIMD one wave is in its MFMA phase while the other
-//     is in its softmax phase and both pipes stay busy.
+//     is in its softmax phase and both pipes stay busy.  The MFMA-phase wave
+//     raises its issue priority (s_setprio), so the matrix pipe is fed first.
 //   * scores are kept in base 2: x = s * scale * log2(e), p = 2^(x - m).
 //   * lazy correction: a tile's weights are formed against the reference
 //     max of an earlier tile, and the row max is not even taken, as long as
@@ -465,8 +466,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       for (int t = 0; t < nt; ++t) {
         softmax(t, t + 2 < nt ? t + 2 : -1, true);
         phase_end(2 * t + 1);
+        __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
+        __builtin_amdgcn_s_setprio(0);
         phase_end(2 * t + 2);
       }
       phase_end(2 * nt + 1);
@@ -478,8 +481,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       for (int t = 0; t < nt; ++t) {
         softmax(t, t + 3 < nt ? t + 3 : -1, false);
         phase_end(2 * t + 2);
+        __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
+        __builtin_amdgcn_s_setprio(0);
         phase_end(2 * t + 3);
       }
     }
