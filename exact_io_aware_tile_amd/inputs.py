@@ -10,7 +10,8 @@ Recipe
   layout, in fixed chunks of ``CHUNK`` elements; chunk ``c`` of stream ``s``
   under seed ``seed`` comes from ``numpy.random.default_rng([seed, s, c])``
   (PCG64).  The values therefore do not depend on how many threads draw them.
-* Streams: q = 0, k = 1, v = 2 (the pages' q, k, v order).  Integer draws
+* Streams: q = 0, k = 1, v = 2 (the pages' q, k, v order), 3 for the new
+  queries of a chunked prefill.  Integer draws
   (lengths, permutations, spike rows) use ``default_rng([seed, 100 + n])``.
 * bf16 tensors are the float32 draws rounded to nearest-even, kept as raw
   ``uint16`` bit patterns; ``bf16_to_f32`` widens them back exactly.
@@ -24,6 +25,7 @@ import numpy as np
 
 CHUNK = 1 << 22
 STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2
+STREAM_QCHUNK = 3  # queries of a chunked prefill
 
 
 def _threads() -> int:
@@ -178,6 +180,26 @@ def paged_case(seed: int, seq_lens, hq: int, hkv: int, d: int, block_size: int =
     }
 
 
+def paged_prefill_case(seed: int, q_lens, k_lens, hq: int, hkv: int, d: int, block_size: int = 16,
+                       pad_blocks: int = 0) -> dict:
+    """Chunks of new queries over a shuffled block pool (bf16).
+
+    Sequence s has k_lens[s] keys in the pool (laid out as in paged_case) and
+    q_lens[s] new queries, packed into q [sum(q_lens), hq, d] with
+    cu_seqlens_q.  The queries are drawn from a stream of their own, so the
+    pool is the same as paged_case's for the same seed and k_lens.
+    """
+    c = paged_case(seed, k_lens, hq, hkv, d, block_size=block_size, pad_blocks=pad_blocks)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    t = int(cu[-1])
+    c["q"] = f32_to_bf16(normal_f32(seed, STREAM_QCHUNK, (t, hq, d)))
+    c.update(cu_seqlens_q=cu, q_lens=q_lens, total_q=t, max_seqlen_q=int(q_lens.max(initial=0)),
+             k_lens=np.asarray(k_lens, dtype=np.int64))
+    return c
+
+
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------
@@ -192,6 +214,10 @@ def workload(n: int) -> dict:
        32 heads, d = 64;
     5. bf16 paged GQA decode, batch 64, 32 q heads / 8 kv heads, d = 128,
        lengths U{1024..32768}, 16-token blocks.
+
+    Beyond these: 6. bf16 chunked prefill over the paged pool, 16 sequences
+    with contexts U{1024..8192}, each adding a causal chunk of its last 512
+    tokens, 32 q heads / 8 kv heads, d = 128.
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -214,5 +240,11 @@ def workload(n: int) -> dict:
         lens = varlen_lengths(5, 64, 1024, 32768)
         c = paged_case(5, lens, 32, 8, 128, block_size=16)
         c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    if n == 6:
+        k_lens = varlen_lengths(6, 16, 1024, 8192)
+        c = paged_prefill_case(6, np.full(16, 512), k_lens, 32, 8, 128, block_size=16)
+        c.update(causal=True,
+                 name="bf16 chunked paged prefill 16 seqs ctx U{1024..8192} chunk 512 Hq=32 Hkv=8 d=128")
         return c
     raise ValueError(f"no workload {n}")

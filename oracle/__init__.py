@@ -50,9 +50,11 @@ def _load(path: str = _LIB):
     lib.oracle_attn_varlen.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P, I, D, P, I64, P, P, I]
     lib.oracle_attn_decode_paged.argtypes = [P, P, P, I, P, P, P, I, P, I, I, I, I, I, I, D, P,
                                              I64, P, P, I]
+    lib.oracle_attn_paged_prefill.argtypes = [P, P, P, I, P, I, P, P, P, I, P, I, I, I, I, I, I, D,
+                                              P, I64, P, P, I]
     lib.oracle_max_threads.argtypes = [I]
     for f in (lib.oracle_attn_dense, lib.oracle_attn_varlen, lib.oracle_attn_decode_paged,
-              lib.oracle_max_threads):
+              lib.oracle_attn_paged_prefill, lib.oracle_max_threads):
         f.restype = I
     if path == _LIB:
         _lib = lib
@@ -181,6 +183,41 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, *, scale: float | Non
         raise ValueError(f"oracle_attn_decode_paged failed with status {st}")
     if r is None:
         return o.reshape(B, Hq, d), lse.reshape(B, Hq)
+    return o, lse
+
+
+def paged_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, *, causal: bool,
+                  scale: float | None = None, rows=None, nthreads: int = 0, lib=None):
+    """Chunked prefill over a paged pool.  q packed [Tq, Hq, d] with
+    cu_seqlens_q [S+1]; pools [num_blocks, Hkv, block, d] (k and v share
+    strides); block_table [S, max_blocks] int32; seq_lens_k [S] int32 (each
+    sequence's whole context).  Causal: query i of a chunk of n sees key t iff
+    t <= i + (seq_lens_k - n).
+
+    With rows=None: o [Hq, Tq, d], lse [Hq, Tq]; else rows are h*Tq + t.
+    """
+    lib = lib or _load()
+    T, Hq, d = q.shape
+    nb, Hkv, bs, _ = k_pool.shape
+    if k_pool.strides != v_pool.strides or k_pool.shape != v_pool.shape:
+        raise ValueError("k and v pools must have the same shape and strides")
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens_k, dtype=np.int32)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r, nr = _rows(rows)
+    n = nr if r is not None else Hq * T
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    qs, ps = _strides(q, 2), _strides(k_pool, 3)
+    st = lib.oracle_attn_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _dtype_code(q), _ptr(cu),
+                                       len(cu) - 1, _ptr(qs), _ptr(ps), _ptr(bt), bt.shape[1], _ptr(sl),
+                                       Hq, Hkv, d, bs, nb, int(bool(causal)), scale, _ptr(r), nr,
+                                       _ptr(o), _ptr(lse), int(nthreads))
+    if st:
+        raise ValueError(f"oracle_attn_paged_prefill failed with status {st}")
+    if r is None:
+        return o.reshape(Hq, T, d), lse.reshape(Hq, T)
     return o, lse
 
 

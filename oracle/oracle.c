@@ -290,3 +290,83 @@ int oracle_attn_decode_paged(const void *q, const void *kpool, const void *vpool
   }
   return bad;
 }
+
+/*
+ * Paged (chunked) prefill: a chunk of new queries per sequence against that
+ * sequence's whole context in a paged pool.  q is packed [Tq, Hq, d] (element
+ * strides {token, head}); sequence s owns query tokens [cu_q[s], cu_q[s+1])
+ * and seq_lens_k[s] logical keys, key t at
+ * pool[block_table[s][t / block]][g][t % block] as in the paged decode
+ * ("S12 FlashAttention", section "What this unlocks beyond speed": the tiles
+ * of a sequence need not be contiguous).  Causal alignment as for dense
+ * attention: query i of the chunk (0-based) sees key t iff
+ * t <= i + (seq_lens_k[s] - chunk length).  Rows are flattened ids
+ * r = h * Tq + t (rows == NULL: all Hq*Tq).
+ */
+int oracle_attn_paged_prefill(const void *q, const void *kpool, const void *vpool, int dtype,
+                              const int32_t *cu_q, int nseq, const int64_t *qs, const int64_t *ps,
+                              const int32_t *block_table, int max_blocks,
+                              const int32_t *seq_lens_k, int Hq, int Hkv, int d, int block_size,
+                              int num_blocks, int causal, double scale, const int64_t *rows,
+                              int64_t nrows, double *o, double *lse, int nthreads) {
+  if (!q || !cu_q || !qs || !ps || !block_table || !seq_lens_k || !o || !lse) return 1;
+  if (nseq < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv || block_size <= 0) return 1;
+  if (cu_q[0] != 0) return 1;
+  int64_t maxlen = 1;
+  for (int s = 0; s < nseq; ++s) {
+    if (cu_q[s + 1] < cu_q[s]) return 1;
+    if (seq_lens_k[s] < 0 || (int64_t)seq_lens_k[s] > (int64_t)max_blocks * block_size) return 1;
+    if (seq_lens_k[s] > maxlen) maxlen = seq_lens_k[s];
+  }
+  if (maxlen > 1 && (!kpool || !vpool)) return 1;
+  const int64_t T = cu_q[nseq];
+  if (!rows) nrows = (int64_t)Hq * T;
+  const int group = Hq / Hkv;
+  int bad = 0;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (size_t)maxlen);
+    int64_t *koff = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxlen);
+    if (!s || !koff) {
+#pragma omp atomic write
+      bad = 2;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < nrows; ++r) {
+        int64_t id = rows ? rows[r] : r;
+        int64_t t = id % (T > 0 ? T : 1), h = id / (T > 0 ? T : 1);
+        if (id < 0 || h >= Hq || T == 0) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        int seq = 0;
+        while (cu_q[seq + 1] <= t) ++seq; /* the sequence holding query token t */
+        int64_t nq = cu_q[seq + 1] - cu_q[seq], nk = seq_lens_k[seq];
+        int64_t i = t - cu_q[seq];
+        int64_t n = causal ? i + 1 + (nk - nq) : nk; /* keys 0 .. n-1 are visible */
+        if (n > nk) n = nk;
+        if (n < 0) n = 0;
+        int64_t g = h / group;
+        int oob = 0;
+        for (int64_t j = 0; j < n; ++j) {
+          int64_t phys = block_table[seq * (int64_t)max_blocks + j / block_size];
+          if (phys < 0 || phys >= num_blocks) oob = 1;
+          koff[j] = phys * ps[0] + g * ps[1] + (j % block_size) * ps[2];
+        }
+        if (oob) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        /* the k and v pools share one addressing, so koff serves both */
+        attend_row(q, kpool, vpool, dtype, d, scale, t * qs[0] + h * qs[1], koff, koff, n, s,
+                   o + r * d, lse + r);
+      }
+    }
+    free(s);
+    free(koff);
+  }
+  return bad;
+}

@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_paged_prefill as C
 from tests import test_oracle_pins as P
 from tests import test_recurrence_cpu as R
 
@@ -40,6 +41,14 @@ MUTANTS = {
     "paged group map": ("int64_t g = h / group, n = seq_lens[b];",
                         "int64_t g = h % Hkv, n = seq_lens[b];"),
     "max not subtracted in weights": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "chunked prefill offset sign": ("int64_t n = causal ? i + 1 + (nk - nq) : nk;",
+                                    "int64_t n = causal ? i + 1 - (nk - nq) : nk;"),
+    "chunked prefill top-left causal": ("int64_t n = causal ? i + 1 + (nk - nq) : nk;",
+                                        "int64_t n = causal ? i + 1 : nk;"),
+    "chunked prefill slot index": ("koff[j] = phys * ps[0] + g * ps[1] + (j % block_size) * ps[2];",
+                                   "koff[j] = phys * ps[0] + g * ps[1] + (j / block_size) * ps[2];"),
+    "chunked prefill block index": ("block_table[seq * (int64_t)max_blocks + j / block_size]",
+                                    "block_table[seq * (int64_t)max_blocks + j % block_size]"),
 }
 
 PINS = [
@@ -60,6 +69,8 @@ PINS = [
     (P.test_bf16_widened_exactly, {}),
     (R.test_tiled_causal_equals_oracle, {}),
     (R.test_paged_equals_oracle, {"seq_len": 95}),
+    (C.test_chunks_equal_dense_over_gathered_keys, {}),
+    (C.test_chunk_longer_than_context_starts_without_keys, {}),
 ]
 
 
