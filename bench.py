@@ -8,8 +8,8 @@ batch 4, 32 heads, N = 2048, d = 128 (seeded synthetic N(0,1) inputs,
 already resident in HBM).  K steps are timed between barrier +
 synchronisation with HIP events on the launch stream.  The paged GQA decode
 workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
-same way and reported in "decode"; the long-context and varlen prefill
-workloads are reported in "extra".
+same way and reported in "decode"; the long-context, varlen and chunked
+paged prefill workloads are reported in "extra".
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "copy"],
+    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -170,6 +170,33 @@ def run_varlen(fa, case, steps, warmup, torch, np):
                          "traffic": None}}
 
 
+def run_paged_prefill(fa, case, steps, warmup, torch, np):
+    q = bf16_dev(case["q"], torch, np)
+    kp = bf16_dev(case["k_pool"], torch, np)
+    vp = bf16_dev(case["v_pool"], torch, np)
+    bt = torch.from_numpy(case["block_table"]).cuda()
+    cu = torch.from_numpy(case["cu_seqlens_q"]).cuda()
+    sl = torch.from_numpy(case["seq_lens"]).cuda()
+    maxk = int(case["seq_lens"].max())
+    o = torch.empty_like(q)
+    lse = torch.empty((case["hq"], case["total_q"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fa_fwd_paged(q, kp, vp, bt, cu, sl, case["max_seqlen_q"], maxk, causal=True, out=o, lse=lse)
+
+    ms, wall_ms = time_steps(step, steps, warmup, torch)
+    pairs = 0
+    for nq, nk in zip(case["q_lens"].tolist(), case["k_lens"].tolist()):
+        i = np.arange(nq, dtype=np.int64)
+        pairs += int(np.clip(i + (nk - nq) + 1, 0, nk).sum())
+    flops = 4.0 * case["d"] * case["hq"] * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tf, "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
+
+
 def run_decode(fa, case, steps, warmup, torch, np):
     q = bf16_dev(case["q"], torch, np)
     kp = bf16_dev(case["k_pool"], torch, np)
@@ -244,6 +271,10 @@ def main():
     if want("varlen", not args.no_extra):
         case = inputs.workload(4)
         out["varlen"] = (case, run_varlen(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2), torch, np))
+    if want("chunked", not args.no_extra):
+        case = inputs.workload(6)
+        out["chunked"] = (case, run_paged_prefill(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2),
+                                                  torch, np))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np))
@@ -282,7 +313,7 @@ def main():
                           "ms_per_step": round(dres["ms"], 4), "algorithmic_bytes": dres["bytes"],
                           "num_splits": dres["num_splits"], "roofline": dres["roofline"]}
     extra = []
-    for key in ("long", "varlen"):
+    for key in ("long", "varlen", "chunked"):
         if key in out:
             c, r = out[key]
             extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",

@@ -206,6 +206,69 @@ FA_EXPORT fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
   return ok();
 }
 
+FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: args is NULL");
+  if (a->num_seqs < 0 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0 || a->heads_q <= 0 ||
+      a->heads_kv <= 0 || a->max_blocks_per_seq < 0 || a->num_blocks < 0)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: negative or zero size");
+  if (a->heads_q % a->heads_kv)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
+                a->heads_kv);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: head_dim %d, supported 64 and 128", a->head_dim);
+  if (a->block_size != fa::kFwdPagedBlock)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: block_size %d, supported %d", a->block_size,
+                fa::kFwdPagedBlock);
+  if ((int64_t)a->max_seqlen_k > (int64_t)a->max_blocks_per_seq * a->block_size)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: max_seqlen_k %d exceeds max_blocks_per_seq * block_size",
+                a->max_seqlen_k);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: scale must be positive and finite");
+  if (a->num_seqs == 0 || a->max_seqlen_q == 0 || a->total_q == 0) return ok();
+  if (!a->q || !a->o || !a->cu_seqlens_q || !a->seq_lens_k)
+    return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: q, o, cu_seqlens_q and seq_lens_k are required");
+  if (a->max_seqlen_k > 0 && (!a->k_pool || !a->v_pool || !a->block_table))
+    return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: pools and block_table are required when max_seqlen_k > 0");
+  if (!strides_ok(a->pool_stride, 3, 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: strides must be non-negative multiples of 8 elements");
+  if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->o))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: q, pools and o must be 16-byte aligned");
+  if (a->pool_stride[2] > fa::kFwdMaxKvRowStrideBf16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: pool token stride above %lld elements",
+                (long long)fa::kFwdMaxKvRowStrideBf16);
+  const int64_t rows = fa::kFwdRowsPerTileBf16;
+  const int64_t qtiles = (a->max_seqlen_q + rows - 1) / rows;
+  if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: grid too large");
+
+  fa::FwdParams p{};
+  p.q = a->q;
+  p.k = a->k_pool;
+  p.v = a->v_pool;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_seqlens = a->cu_seqlens_q;
+  p.q_bs = 0, p.q_ss = a->q_stride[0], p.q_hs = a->q_stride[1];
+  p.o_bs = 0, p.o_ss = a->o_stride[0], p.o_hs = a->o_stride[1];
+  p.batch = a->num_seqs;
+  p.seqlen_q = a->max_seqlen_q;
+  p.seqlen_k = a->max_seqlen_k;
+  p.total_tokens = a->total_q;
+  p.heads_q = a->heads_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.num_qtiles = (int32_t)qtiles;
+  p.causal = a->causal ? 1 : 0;
+  p.scale_log2 = scale_log2(a->scale);
+  p.paged = 1;
+  p.block_table = a->block_table;  // with max_seqlen_k == 0 neither table nor pools are read
+  p.seq_lens_k = a->seq_lens_k;
+  p.max_blocks = a->max_blocks_per_seq;
+  p.p_bs = a->pool_stride[0], p.p_hs = a->pool_stride[1], p.p_ts = a->pool_stride[2];
+  const hipError_t e = fa::launch_fwd_bf16(p, a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_paged: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) {
   if (check_decode(a) != FA_OK) return 0;
   const int parts = decode_parts(a);

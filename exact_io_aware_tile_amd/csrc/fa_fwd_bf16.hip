@@ -129,7 +129,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = kBc * D;            // elements per K or V tile
@@ -170,7 +170,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 
   int nq, nk;
   int64_t q_base, k_base, v_base, o_base, lse_base;
-  if (p.cu_seqlens) {
+  if (PAGED) {
+    // new queries packed by cu_seqlens; keys of the sequence in the pools
+    const int s0 = p.cu_seqlens[b];
+    nq = p.cu_seqlens[b + 1] - s0;
+    nk = min(max(p.seq_lens_k[b], 0), p.seqlen_k);
+    q_base = (int64_t)s0 * p.q_ss;
+    k_base = 0;
+    v_base = 0;
+    o_base = (int64_t)s0 * p.o_ss;
+    lse_base = (int64_t)h * p.total_tokens + s0;
+  } else if (p.cu_seqlens) {
     const int s0 = p.cu_seqlens[b];
     const int s1 = p.cu_seqlens[b + 1];
     nq = nk = s1 - s0;
@@ -192,8 +202,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   if (q0 >= nq) return;  // uniform over the workgroup
   const int g = h / p.group;
   q_base += (int64_t)h * p.q_hs;
-  k_base += (int64_t)g * p.k_hs;
-  v_base += (int64_t)g * p.v_hs;
+  k_base += (int64_t)g * (PAGED ? p.p_hs : p.k_hs);
+  v_base += (int64_t)g * (PAGED ? p.p_hs : p.v_hs);
   o_base += (int64_t)h * p.o_hs;
   const int off = nk - nq;  // causal: key j visible from row i iff j <= i + off
 
@@ -239,33 +249,70 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   const int drow = lane / CH;
   const int dpch = lane % CH;
   const int wq = wave & 3;
+  // Paged: wave w's rows 16(w%4) .. 16(w%4)+15 of a tile are exactly one
+  // 16-token block, fetched from the pool block the table names; the lane
+  // offsets are then relative to that block.
+  static_assert(!PAGED || RPW == kFwdPagedBlock, "one pool block per wave and tile");
+  const int64_t kv_row_k = PAGED ? p.p_ts : p.k_ss;
+  const int64_t kv_row_v = PAGED ? p.p_ts : p.v_ss;
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = wq * RPW + i * RPI + drow;
-    koff[i] = (uint32_t)(((int64_t)r * p.k_ss + swz_k(CH, r, dpch) * 8) * 2);
-    voff[i] = (uint32_t)(((int64_t)r * p.v_ss + swz_v(CH, r, dpch) * 8) * 2);
+    const int r = wq * RPW + i * RPI + drow;      // row of the tile in LDS
+    const int rs = PAGED ? i * RPI + drow : r;    // ... in the source
+    koff[i] = (uint32_t)(((int64_t)rs * kv_row_k + swz_k(CH, r, dpch) * 8) * 2);
+    voff[i] = (uint32_t)(((int64_t)rs * kv_row_v + swz_v(CH, r, dpch) * 8) * 2);
   }
-  // Instruction i of this wave's share of operand V_OP (K when false) of a tile.
-  auto dma_one = [&](int tile, bool v_op, int i) {
+  // Paged: the wave's block of tile `tile` (a block past the last key is
+  // replaced by the last key's block).
+  auto wave_block = [&](int tile) {
+    return __builtin_amdgcn_readfirstlane(min(tile * (kBc / kFwdPagedBlock) + wq, (nk - 1) / kFwdPagedBlock));
+  };
+  // Its pool block, read from the table through the scalar cache (the table
+  // is constant during the launch; a vector load would be counted with the
+  // DMA loads in flight and waiting for it would drain them).
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (PAGED ? (int64_t)b * p.max_blocks : 0));
+  auto pool_block = [&](int tile) -> int32_t {
+    if (!PAGED || tile < 0) return 0;
+    return table[wave_block(tile)];
+  };
+  // Instruction i of this wave's share of operand V_OP (K when false) of a
+  // tile; PHYS is pool_block(tile) when paged.
+  auto dma_one = [&](int tile, bool v_op, int i, int32_t phys) {
     const int st = tile % kStages;
-    const uint16_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
     const int r0 = wq * RPW + i * RPI;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
     const int rows_left = nk - tile * kBc;  // uniform
     uint32_t off = v_op ? voff[i] : koff[i];
-    if (rows_left < kBc) {
-      const int r = r0 + drow;
-      const int rk = min(r, rows_left - 1);
-      off = v_op ? (uint32_t)(((int64_t)rk * p.v_ss + swz_v(CH, r, dpch) * 8) * 2)
-                 : (uint32_t)(((int64_t)rk * p.k_ss + swz_k(CH, r, dpch) * 8) * 2);
+    if (PAGED) {
+      // In the last tile rows past the last key re-read that key, in the
+      // last key's block.
+      if (rows_left < kBc) {
+        const int r = r0 + drow;
+        const int key = tile * kBc + min(r, rows_left - 1);
+        const int rb = key - wave_block(tile) * kFwdPagedBlock;
+        off = v_op ? (uint32_t)(((int64_t)rb * p.p_ts + swz_v(CH, r, dpch) * 8) * 2)
+                   : (uint32_t)(((int64_t)rb * p.p_ts + swz_k(CH, r, dpch) * 8) * 2);
+      }
+      const uint16_t* base = (v_op ? vg : kg) + (int64_t)phys * p.p_bs;
+      dma_16b(base, off, lds);
+    } else {
+      const uint16_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
+      if (rows_left < kBc) {
+        const int r = r0 + drow;
+        const int rk = min(r, rows_left - 1);
+        off = v_op ? (uint32_t)(((int64_t)rk * p.v_ss + swz_v(CH, r, dpch) * 8) * 2)
+                   : (uint32_t)(((int64_t)rk * p.k_ss + swz_k(CH, r, dpch) * 8) * 2);
+      }
+      dma_16b(base, off, lds);
     }
-    dma_16b(base, off, lds);
   };
   auto dma_op = [&](int tile, bool v_op) {
+    const int32_t phys = pool_block(tile);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i);
+    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i, phys);
   };
 
   // Prologue loads: group 0 takes K, group 1 V.  Tile 0 flies while the Q
@@ -313,13 +360,13 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // per 1 KB instruction per CU and a wave stalls while it is busy, so the
   // loads are spaced out and issued only by the group whose matrix pipe is
   // idle.
-  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v) {
+  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v, int32_t dma_phys) {
     float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       if (dma_tile >= 0 && kc % (4 / IPW) == 0) {
         __builtin_amdgcn_sched_barrier(0);
-        dma_one(dma_tile, dma_v, kc / (4 / IPW));
+        dma_one(dma_tile, dma_v, kc / (4 / IPW), dma_phys);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int kb = kc >> 1;
@@ -340,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
   };
 
-  auto softmax = [&](int t, int dma_tile, bool dma_v) {
+  auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
     if (need_mask) {
@@ -359,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     // to the exact step, which takes the row max, moves the reference and
     // recomputes the weights.
     float ps;
-    weights(m_run, ps, dma_tile, dma_v);
+    weights(m_run, ps, dma_tile, dma_v, dma_phys);
     corr = __any(!(ps <= kLazyBound));
     if (corr) {
       float mx[4];
@@ -374,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false, 0);
     }
     l_run += ps;
   };
@@ -460,31 +507,40 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     wait_vmcnt<0>();
     if (nt > 1) dma_op(1, grp != 0);
     lds_barrier();
+    // Paged: the table entry for the DMA of the next softmax phase is read
+    // at the end of the MFMA phase before it, when no LDS read is pending
+    // (both count on the same counter), and arrives during the barrier.
     if (grp == 0) {
       scores(0);
+      int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 2 < nt ? t + 2 : -1, true);
+        softmax(t, t + 2 < nt ? t + 2 : -1, true, ph);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        ph = pool_block(t + 3 < nt ? t + 3 : -1);
         phase_end(2 * t + 2);
       }
       phase_end(2 * nt + 1);
     } else {
       if (2 < nt) dma_op(2, false);
+      int32_t ph = pool_block(3 < nt ? 3 : -1);
       phase_end(0);
       scores(0);
       phase_end(1);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 3 < nt ? t + 3 : -1, false);
+        softmax(t, t + 3 < nt ? t + 3 : -1, false, ph);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        ph = pool_block(t + 4 < nt ? t + 4 : -1);
         phase_end(2 * t + 3);
       }
     }
@@ -525,7 +581,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int64_t nwg = (int64_t)p.num_qtiles * p.heads_q * p.batch;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  if (p.paged)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

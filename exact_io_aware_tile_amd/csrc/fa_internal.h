@@ -13,6 +13,8 @@ constexpr int kFwdRowsPerTileF32 = 128;
 // The bf16 prefill kernel addresses rows inside a 64-key tile with 32-bit
 // byte offsets: key/value row strides (elements) are limited to 2^24.
 constexpr int64_t kFwdMaxKvRowStrideBf16 = int64_t(1) << 24;
+// Paged prefill reads 16-token blocks.
+constexpr int kFwdPagedBlock = 16;
 
 // One prefill launch: dense batched attention or packed variable-length
 // sequences.  All strides are in elements.
@@ -36,6 +38,16 @@ struct FwdParams {
   int32_t num_qtiles;    // query tiles per (sequence, head)
   int32_t causal;
   float scale_log2;      // scale * log2(e): scores are kept in base 2
+  // Paged keys and values (chunked prefill, bf16): when `paged` is set,
+  // q / o / lse are packed by cu_seqlens (the new queries of each sequence),
+  // k / v point at the two pools, and key t of sequence s is token t % 16
+  // of pool block block_table[s * max_blocks + t / 16]; the sequence has
+  // seq_lens_k[s] keys (clamped to [0, seqlen_k]).
+  int32_t paged;
+  const int32_t* block_table;
+  const int32_t* seq_lens_k;
+  int32_t max_blocks;
+  int64_t p_bs, p_hs, p_ts;  // pool strides: block, head, token
 };
 
 // Paged decode: query heads per kv head (one wave serves the whole group),

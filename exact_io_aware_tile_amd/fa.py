@@ -8,6 +8,8 @@ is raised.
 Layouts (see include/fa.h):
     fa_fwd:          q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o like q, lse [B, Hq, Nq]
     fa_fwd_varlen:   q [T, Hq, d], k/v [T, Hkv, d], cu_seqlens int32 [S+1] -> o, lse [Hq, T]
+    fa_fwd_paged:    q [Tq, Hq, d] (chunks packed by cu_seqlens_q int32 [S+1]), pools and
+                     block_table as for decode, seq_lens_k int32 [S] -> o like q, lse [Hq, Tq]
     fa_decode_paged: q [B, Hq, d], pools [blocks, Hkv, 16, d] (or any strides with d
                      contiguous), block_table int32 [B, max_blocks], seq_lens int32 [B]
                      -> o [B, Hq, d], lse [B, Hq]
@@ -55,7 +57,16 @@ class DecodePagedArgs(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
-SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_paged", "fa_decode_paged_workspace_size",
+class FwdPagedArgs(ctypes.Structure):
+    _fields_ = [("q", _P), ("k_pool", _P), ("v_pool", _P), ("pool_stride", _I64 * 3),
+                ("block_table", _P), ("cu_seqlens_q", _P), ("seq_lens_k", _P), ("o", _P), ("lse", _P),
+                ("q_stride", _I64 * 2), ("o_stride", _I64 * 2),
+                ("num_seqs", _I32), ("total_q", _I32), ("max_seqlen_q", _I32), ("max_seqlen_k", _I32),
+                ("heads_q", _I32), ("heads_kv", _I32), ("head_dim", _I32), ("block_size", _I32),
+                ("max_blocks_per_seq", _I32), ("num_blocks", _I32), ("scale", _F), ("causal", _I32)]
+
+
+SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -79,6 +90,8 @@ def lib(path: str = LIB_PATH):
     L.fa_fwd.restype = ctypes.c_int
     L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), _P]
     L.fa_fwd_varlen.restype = ctypes.c_int
+    L.fa_fwd_paged.argtypes = [ctypes.POINTER(FwdPagedArgs), _P]
+    L.fa_fwd_paged.restype = ctypes.c_int
     L.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
     L.fa_decode_paged.restype = ctypes.c_int
     L.fa_decode_paged_workspace_size.argtypes = [ctypes.POINTER(DecodePagedArgs)]
@@ -188,6 +201,54 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = True,
     return out, lse
 
 
+def _fwd_paged_args(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,
+                    causal, scale):
+    Tq, Hq, d = q.shape
+    nb, Hkv, bs, _ = k_pool.shape
+    if tuple(k_pool.stride()) != tuple(v_pool.stride()) or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must share shape and strides")
+    a = FwdPagedArgs()
+    a.q, a.k_pool, a.v_pool = _ptr(q), _ptr(k_pool), _ptr(v_pool)
+    a.pool_stride[:] = list(k_pool.stride()[:3])
+    a.block_table, a.cu_seqlens_q, a.seq_lens_k = _ptr(block_table), _ptr(cu_seqlens_q), _ptr(seq_lens_k)
+    a.q_stride[:] = list(q.stride()[:2])
+    a.num_seqs, a.total_q = cu_seqlens_q.numel() - 1, Tq
+    a.max_seqlen_q, a.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    a.heads_q, a.heads_kv, a.head_dim, a.block_size = Hq, Hkv, d, bs
+    a.max_blocks_per_seq = block_table.shape[1] if block_table is not None else 0
+    a.num_blocks = nb
+    a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a.causal = int(bool(causal))
+    return a
+
+
+def fa_fwd_paged(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q: int,
+                 max_seqlen_k: int, *, causal: bool = True, scale: float | None = None, out=None, lse=None,
+                 return_lse: bool = True, stream=None):
+    """Chunked prefill over a paged KV pool (bf16).  ``max_seqlen_q`` and
+    ``max_seqlen_k`` are host-side bounds.  Returns (o, lse)."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q), ("seq_lens_k", seq_lens_k)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise TypeError("fa_fwd_paged takes bf16 q and pools")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
+    Tq, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    a = _fwd_paged_args(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,
+                        causal, scale)
+    a.o, a.lse = _ptr(out), _ptr(lse)
+    a.o_stride[:] = list(out.stride()[:2])
+    _check(lib().fa_fwd_paged(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
 def _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, num_splits):
     B, Hq, d = q.shape
     nb, Hkv, bs, _ = k_pool.shape
@@ -227,6 +288,8 @@ def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, 
     _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse)
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty_like(q)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_OK = 0,
@@ -128,6 +128,55 @@ typedef struct {
 } fa_fwd_varlen_args;
 
 fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
+
+/*
+ * fa_fwd_paged -- chunked prefill over a paged KV pool: every sequence
+ * brings a chunk of new queries that attends to all of the sequence's keys
+ * in the pool (the cached prefix and the chunk's own keys, which the caller
+ * has already written there).  The tiles of keys and values are fetched
+ * through the block table, as "S12 FlashAttention"
+ * (llminference.xinbetween.com), "What this unlocks beyond speed", has the
+ * tiled loop do for paged memory; queries are packed without padding as in
+ * "Varlen Is the Quiet Superpower" (repo-explainer.com).
+ *
+ *   q   [total_q, heads_q, head_dim] bf16, strides q_stride = {token, head};
+ *       sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]).
+ *   k_pool, v_pool, pool_stride, block_table, num_blocks: as for
+ *       fa_decode_paged; the token stride is at most 2^24 elements.
+ *   cu_seqlens_q: DEVICE int32 [num_seqs + 1], cu[0] = 0, non-decreasing,
+ *       cu[num_seqs] = total_q.
+ *   seq_lens_k: DEVICE int32 [num_seqs]: keys of sequence s, the chunk's
+ *       own included; values outside [0, max_seqlen_k] are clamped to it.
+ *   o   [total_q, heads_q, head_dim] bf16, strides o_stride (written)
+ *   lse [heads_q, total_q] fp32 contiguous (written; may be NULL)
+ *   max_seqlen_q: HOST-side upper bound on every chunk length (it sizes the
+ *       grid; a longer chunk is processed only up to max_seqlen_q queries).
+ *   max_seqlen_k: HOST-side upper bound on seq_lens_k, at most
+ *       max_blocks_per_seq * block_size.
+ *
+ * With causal != 0 query i of a chunk of n_q queries over n_k keys sees
+ * keys j <= i + n_k - n_q: the chunk is the last n_q positions of the
+ * sequence.  A query that sees no key (a chunk longer than its keys, or
+ * n_k = 0) gets o = 0 and lse = -inf.  A chunk of one query is a decode
+ * step.  Supported: bf16, head_dim 64 or 128, block_size 16.
+ */
+typedef struct {
+  const void *q;
+  const void *k_pool, *v_pool;
+  int64_t pool_stride[3];
+  const int32_t *block_table;
+  const int32_t *cu_seqlens_q;
+  const int32_t *seq_lens_k;
+  void *o;
+  float *lse;
+  int64_t q_stride[2], o_stride[2];
+  int32_t num_seqs, total_q, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, head_dim, block_size,
+      max_blocks_per_seq, num_blocks;
+  float scale;
+  int32_t causal;
+} fa_fwd_paged_args;
+
+fa_status fa_fwd_paged(const fa_fwd_paged_args *args, void *stream);
 
 /*
  * fa_decode_paged -- one query token per sequence over a paged KV pool

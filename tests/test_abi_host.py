@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 2
+    assert L.fa_abi_version() == declared == 3
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -65,6 +65,7 @@ def test_abi_version_and_strings(L):
 STRUCTS = {
     "fa_fwd_args": fa.FwdArgs,
     "fa_fwd_varlen_args": fa.FwdVarlenArgs,
+    "fa_fwd_paged_args": fa.FwdPagedArgs,
     "fa_decode_paged_args": fa.DecodePagedArgs,
 }
 
@@ -171,6 +172,53 @@ def test_varlen_empty_is_noop(L):
     for kw in (dict(num_seqs=0), dict(max_seqlen=0), dict(total_tokens=0)):
         a = varlen_args(q=None, k=None, v=None, o=None, cu_seqlens=None, **kw)
         assert L.fa_fwd_varlen(ctypes.byref(a), None) == fa.FA_OK
+
+
+def paged_args(**kw):
+    a = fa.FwdPagedArgs()
+    a.num_seqs, a.total_q, a.max_seqlen_q, a.max_seqlen_k = 3, 40, 20, 300
+    a.heads_q, a.heads_kv, a.head_dim, a.block_size = 8, 2, 128, 16
+    a.max_blocks_per_seq, a.num_blocks = 20, 64
+    a.scale, a.causal = 0.088, 1
+    a.q = a.k_pool = a.v_pool = a.block_table = a.cu_seqlens_q = a.seq_lens_k = a.o = 0x1000
+    a.pool_stride[:] = [2 * 16 * 128, 16 * 128, 128]
+    a.q_stride[:] = [8 * 128, 128]
+    a.o_stride[:] = [8 * 128, 128]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=7), fa.FA_ERR_BAD_SHAPE),
+    (dict(total_q=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(block_size=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(max_seqlen_k=20 * 16 + 1), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(cu_seqlens_q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(seq_lens_k=None), fa.FA_ERR_NULL_POINTER),
+    (dict(block_table=None), fa.FA_ERR_NULL_POINTER),
+    (dict(k_pool=None), fa.FA_ERR_NULL_POINTER),
+    (dict(q_stride=[8 * 128, 100]), fa.FA_ERR_BAD_SHAPE),
+    (dict(o=0x1004), fa.FA_ERR_BAD_SHAPE),
+    (dict(pool_stride=[1 << 40, 16 * 128, (1 << 24) + 8]), fa.FA_ERR_UNSUPPORTED),
+])
+def test_paged_prefill_rejects_before_launch(L, kw, status):
+    a = paged_args(**kw)
+    assert L.fa_fwd_paged(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_paged_prefill_empty_is_noop(L):
+    for kw in (dict(num_seqs=0), dict(max_seqlen_q=0), dict(total_q=0)):
+        a = paged_args(q=None, k_pool=None, v_pool=None, block_table=None, cu_seqlens_q=None,
+                       seq_lens_k=None, o=None, **kw)
+        assert L.fa_fwd_paged(ctypes.byref(a), None) == fa.FA_OK
+    assert L.fa_fwd_paged(None, None) == fa.FA_ERR_NULL_POINTER
 
 
 def decode_args(**kw):

@@ -350,3 +350,109 @@ def test_decode_workload_sampled(gpu):
     og = host(o).reshape(B * H, -1)[rows]
     lg = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
     check(og, lg, o_ref, lse_ref, "bf16", "decode workload sampled")
+
+
+# --------------------------------------------------------------------------
+# chunked prefill over the paged pool
+# --------------------------------------------------------------------------
+def paged_prefill_gpu(fa, case, causal=True, k_pool=None, v_pool=None, table=None):
+    q = dev(case["q"], "bf16")
+    kp = dev(case["k_pool"], "bf16") if k_pool is None else k_pool
+    vp = dev(case["v_pool"], "bf16") if v_pool is None else v_pool
+    bt = torch.from_numpy(case["block_table"]).cuda() if table is None else table
+    cu = torch.from_numpy(case["cu_seqlens_q"]).cuda()
+    sl = torch.from_numpy(case["seq_lens"]).cuda()
+    o, lse = fa.fa_fwd_paged(q, kp, vp, bt, cu, sl, case["max_seqlen_q"], int(case["seq_lens"].max(initial=0)),
+                             causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_paged_prefill(fa, case, causal, rows=None):
+    o, lse = paged_prefill_gpu(fa, case, causal)
+    o_ref, lse_ref = oracle.paged_prefill(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                          case["cu_seqlens_q"], case["seq_lens"], causal=causal, rows=rows)
+    og = host(o).transpose(1, 0, 2)  # [Hq, Tq, d]
+    lg = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        og = og.reshape(-1, og.shape[-1])[rows]
+        lg = lg.reshape(-1)[rows]
+    return og, lg, o_ref, lse_ref
+
+
+# chunk of one query, chunk = whole context, chunk longer than its keys,
+# a sequence without keys, one without queries, several key tiles with
+# ragged tails and several query tiles
+PAGED_Q = [1, 130, 7, 5, 64, 300, 6, 257, 0]
+PAGED_K = [1, 333, 7, 0, 1000, 300, 4, 600, 40]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("group", [1, 4])
+def test_paged_prefill_parity(gpu, group, d, causal):
+    case = inputs.paged_prefill_case(400 + 10 * group + d, PAGED_Q, PAGED_K, 2 * group, 2, d, pad_blocks=1)
+    og, lg, o_ref, lse_ref = run_paged_prefill(gpu, case, causal)
+    check(og, lg, o_ref, lse_ref, "bf16", f"paged prefill group={group} d={d} causal={causal}")
+
+
+def test_paged_prefill_whole_context_is_varlen_bitwise(gpu):
+    # a chunk that is the whole context reads exactly the keys the packed
+    # kernel reads, in the same tiles: identical bits
+    lens = [300, 64, 17, 700]
+    case = inputs.paged_prefill_case(410, lens, lens, 8, 2, 128)
+    o1, l1 = paged_prefill_gpu(gpu, case, causal=True)
+    bs = case["block_size"]
+    kp, vp = dev(case["k_pool"], "bf16"), dev(case["v_pool"], "bf16")
+    ks, vs = [], []
+    for s, L in enumerate(lens):
+        t = torch.arange(L, device="cuda")
+        phys = torch.from_numpy(case["block_table"][s]).cuda().long()[t // bs]
+        ks.append(kp[phys, :, t % bs])
+        vs.append(vp[phys, :, t % bs])
+    k, v = torch.cat(ks).contiguous(), torch.cat(vs).contiguous()
+    cu = torch.from_numpy(case["cu_seqlens_q"]).cuda()
+    o2, l2 = gpu.fa_fwd_varlen(dev(case["q"], "bf16"), k, v, cu, max(lens), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+
+
+def test_paged_prefill_pool_order_bitwise(gpu):
+    q_lens, k_lens = [512, 33, 200], [2000, 33, 1500]
+    case = inputs.paged_prefill_case(420, q_lens, k_lens, 16, 4, 128)
+    o1, l1 = paged_prefill_gpu(gpu, case)
+    bt = case["block_table"]
+    order = np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(k_lens)]).astype(np.int64)
+    idx = torch.from_numpy(order).cuda()
+    kp = dev(case["k_pool"], "bf16").index_select(0, idx)
+    vp = dev(case["v_pool"], "bf16").index_select(0, idx)
+    ident = np.full_like(bt, -1)
+    pos = 0
+    for b, L in enumerate(k_lens):
+        nb = (L + 15) // 16
+        ident[b, :nb] = np.arange(pos, pos + nb)
+        pos += nb
+    o2, l2 = paged_prefill_gpu(gpu, case, k_pool=kp, v_pool=vp, table=torch.from_numpy(ident).cuda())
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+    # token-major pool [blocks, 16, Hkv, d] viewed with the same logical shape
+    kt = dev(np.ascontiguousarray(case["k_pool"].transpose(0, 2, 1, 3)), "bf16").transpose(1, 2)
+    vt = dev(np.ascontiguousarray(case["v_pool"].transpose(0, 2, 1, 3)), "bf16").transpose(1, 2)
+    o3, l3 = paged_prefill_gpu(gpu, case, k_pool=kt, v_pool=vt)
+    assert torch.equal(o1, o3)
+    assert torch.equal(l1, l3)
+
+
+def test_paged_prefill_workload_sampled(gpu):
+    case = inputs.workload(6)
+    T, H = case["total_q"], case["hq"]
+    rng = np.random.default_rng(6)
+    rows = set(rng.integers(0, H * T, size=256).tolist())
+    cu = case["cu_seqlens_q"]
+    for s in range(len(cu) - 1):  # first and last query of every chunk
+        for t in (cu[s], cu[s + 1] - 1):
+            rows.add(int(rng.integers(0, H)) * T + int(t))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    og, lg, o_ref, lse_ref = run_paged_prefill(gpu, case, True, rows=rows)
+    check(og, lg, o_ref, lse_ref, "bf16", "paged prefill workload sampled rows")
