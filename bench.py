@@ -34,6 +34,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "decode": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
+    "chunked": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
 }
 
 
@@ -194,7 +195,7 @@ def run_paged_prefill(fa, case, steps, warmup, torch, np):
     return {"ms": ms, "tflops": tf, "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": measured_traffic("chunked")}}
 
 
 def run_decode(fa, case, steps, warmup, torch, np):
