@@ -15,6 +15,9 @@ Recipe
   (lengths, permutations, spike rows) use ``default_rng([seed, 100 + n])``.
 * bf16 tensors are the float32 draws rounded to nearest-even, kept as raw
   ``uint16`` bit patterns; ``bf16_to_f32`` widens them back exactly.
+* fp8 tensors are FP8 E4M3 codes (``uint8``) of the float32 draws divided by
+  a per-tensor descale factor amax / 448 (float32), rounded to nearest-even
+  and saturated at +-448; the tensor they stand for is descale * value(code).
 """
 from __future__ import annotations
 
@@ -88,6 +91,40 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+# The 127 non-negative finite E4M3 values in code order (codes 0x00..0x7E):
+# subnormals m * 2^-9, then (1 + m/8) * 2^(e-7); increasing with the code.
+_E4M3_POS = np.array([m * 2.0**-9 if e == 0 else (1 + m / 8) * 2.0**(e - 7)
+                      for e in range(16) for m in range(8)][:127], dtype=np.float64)
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 to FP8 E4M3 codes (uint8): nearest value, ties to the even
+    code, magnitudes above 448 saturated to 448.  Inputs are finite."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 126)   # first value >= a
+    lo = hi - 1
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a >= E4M3_MAX, 126, code).astype(np.uint8)
+    return np.where(np.signbit(np.asarray(x, dtype=np.float32)), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def e4m3_to_f32(c: np.ndarray) -> np.ndarray:
+    """Widen E4M3 codes (uint8, no NaN codes) to float32, exactly."""
+    c = np.asarray(c, dtype=np.uint8)
+    v = _E4M3_POS[np.minimum(c & np.uint8(0x7F), 126)].astype(np.float32)
+    return np.where(c >= 0x80, -v, v)
+
+
+def to_fp8(x: np.ndarray):
+    """Per-tensor scaled E4M3: (codes, descale) with descale = amax / 448."""
+    amax = float(np.max(np.abs(x))) if x.size else 1.0
+    descale = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
+    return f32_to_e4m3(np.asarray(x, dtype=np.float32) / descale), descale
+
+
 def _maybe_bf16(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return x
@@ -122,6 +159,16 @@ def dense_case(seed: int, batch: int, nq: int, nk: int, hq: int, hkv: int, d: in
         "dtype": dtype, "batch": batch, "nq": nq, "nk": nk, "hq": hq, "hkv": hkv, "d": d,
         "spikes": spikes,
     }
+
+
+def fp8_case(seed: int, batch: int, nq: int, nk: int, hq: int, hkv: int, d: int) -> dict:
+    """Seeded dense case in FP8 E4M3 with per-tensor descale factors (the same
+    float32 draws as ``dense_case``)."""
+    q8, qd = to_fp8(normal_f32(seed, STREAM_Q, (batch, nq, hq, d)))
+    k8, kd = to_fp8(normal_f32(seed, STREAM_K, (batch, nk, hkv, d)))
+    v8, vd = to_fp8(normal_f32(seed, STREAM_V, (batch, nk, hkv, d)))
+    return {"q": q8, "k": k8, "v": v8, "descale": (qd, kd, vd), "dtype": "fp8",
+            "batch": batch, "nq": nq, "nk": nk, "hq": hq, "hkv": hkv, "d": d}
 
 
 # --------------------------------------------------------------------------
@@ -217,7 +264,8 @@ def workload(n: int) -> dict:
 
     Beyond these: 6. bf16 chunked prefill over the paged pool, 16 sequences
     with contexts U{1024..8192}, each adding a causal chunk of its last 512
-    tokens, 32 q heads / 8 kv heads, d = 128.
+    tokens, 32 q heads / 8 kv heads, d = 128; 7. workload 2 in FP8 E4M3 with
+    per-tensor descale factors.
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -240,6 +288,10 @@ def workload(n: int) -> dict:
         lens = varlen_lengths(5, 64, 1024, 32768)
         c = paged_case(5, lens, 32, 8, 128, block_size=16)
         c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    if n == 7:
+        c = fp8_case(7, 4, 2048, 2048, 32, 32, 128)
+        c.update(causal=True, name="fp8 e4m3 causal MHA prefill B=4 H=32 N=2048 d=128")
         return c
     if n == 6:
         k_lens = varlen_lengths(6, 16, 1024, 8192)

@@ -53,6 +53,8 @@ def _load(path: str = _LIB):
     lib.oracle_attn_paged_prefill.argtypes = [P, P, P, I, P, I, P, P, P, I, P, I, I, I, I, I, I, D,
                                               P, I64, P, P, I]
     lib.oracle_max_threads.argtypes = [I]
+    lib.oracle_decode_e4m3.argtypes = [P, P, I64]
+    lib.oracle_decode_e4m3.restype = None
     for f in (lib.oracle_attn_dense, lib.oracle_attn_varlen, lib.oracle_attn_decode_paged,
               lib.oracle_attn_paged_prefill, lib.oracle_max_threads):
         f.restype = I
@@ -226,3 +228,30 @@ def visible_pairs_dense(nq: int, nk: int, causal: bool) -> int:
     if not causal:
         return nq * nk
     return sum(max(0, min(nk, i + (nk - nq) + 1)) for i in range(nq))
+
+
+def decode_e4m3(codes, *, lib=None) -> np.ndarray:
+    """FP8 E4M3 codes (uint8) -> their exact values in float64 (see
+    oracle_decode_e4m3 for the format)."""
+    L = lib or _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    L.oracle_decode_e4m3(_ptr(c), _ptr(out), c.size)
+    return out
+
+
+def fp8_dense(q8, k8, v8, descale, *, causal: bool, scale: float | None = None, rows=None,
+              nthreads: int = 0, lib=None):
+    """Dense attention over FP8 E4M3 inputs with per-tensor descale factors.
+
+    The inputs stand for the real tensors q = descale[0] * value(q8), k =
+    descale[1] * value(k8), v = descale[2] * value(v8); the result is the
+    exact attention of those (``dense`` on the widened, scaled tensors), with
+    the same layouts and return values as ``dense``.  The scale defaults to
+    1/sqrt(d).
+    """
+    qd, kd, vd = (float(x) for x in descale)
+    q = decode_e4m3(q8, lib=lib) * qd
+    k = decode_e4m3(k8, lib=lib) * kd
+    v = decode_e4m3(v8, lib=lib) * vd
+    return dense(q, k, v, causal=causal, scale=scale, rows=rows, nthreads=nthreads, lib=lib)

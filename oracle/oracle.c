@@ -109,6 +109,30 @@ static int set_threads(int nthreads) {
 int oracle_max_threads(int nthreads) { return set_threads(nthreads); }
 
 /*
+ * FP8 E4M3 codes to their values ("S12 FlashAttention", "Production notes /
+ * In production": FlashAttention-3 adds FP8 inputs; the format itself is the
+ * OCP 8-bit floating point E4M3 format, which the pages do not restate):
+ * bit 7 is the sign, bits 6..3 the exponent with bias 7, bits 2..0 the
+ * mantissa.  Exponent 0 holds the subnormals m * 2^-9; exponent 15 with
+ * mantissa 7 is NaN (there are no infinities), so the largest finite value
+ * is 1.75 * 2^8 = 448.  Every value is exact in double.
+ */
+void oracle_decode_e4m3(const uint8_t *src, double *dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    const int c = src[i];
+    const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+      v = NAN;
+    else if (e == 0)
+      v = ldexp((double)m, -9);
+    else
+      v = ldexp(8.0 + m, e - 10); /* (1 + m/8) * 2^(e-7) */
+    dst[i] = sign ? -v : v;
+  }
+}
+
+/*
  * Dense batched attention.  q is [B, Nq, Hq, d], k and v are [B, Nk, Hkv, d],
  * addressed with element strides {batch, seq, head} (d is contiguous).
  * Rows are flattened ids r = (b * Hq + h) * Nq + i; rows == NULL means all

@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_fp8 as F
 from tests import test_oracle_paged_prefill as C
 from tests import test_oracle_pins as P
 from tests import test_recurrence_cpu as R
@@ -49,6 +50,10 @@ MUTANTS = {
                                    "koff[j] = phys * ps[0] + g * ps[1] + (j / block_size) * ps[2];"),
     "chunked prefill block index": ("block_table[seq * (int64_t)max_blocks + j / block_size]",
                                     "block_table[seq * (int64_t)max_blocks + j % block_size]"),
+    "e4m3 exponent bias": ("v = ldexp(8.0 + m, e - 10);", "v = ldexp(8.0 + m, e - 11);"),
+    "e4m3 subnormal scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "e4m3 implicit bit dropped": ("v = ldexp(8.0 + m, e - 10);", "v = ldexp((double)m, e - 10);"),
+    "e4m3 sign ignored": ("dst[i] = sign ? -v : v;", "dst[i] = v;"),
 }
 
 PINS = [
@@ -71,6 +76,8 @@ PINS = [
     (R.test_paged_equals_oracle, {"seq_len": 95}),
     (C.test_chunks_equal_dense_over_gathered_keys, {}),
     (C.test_chunk_longer_than_context_starts_without_keys, {}),
+    (F.test_decode_all_codes_match_torch, {}),
+    (F.test_decode_closed_forms, {}),
 ]
 
 
