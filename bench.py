@@ -8,8 +8,9 @@ batch 4, 32 heads, N = 2048, d = 128 (seeded synthetic N(0,1) inputs,
 already resident in HBM).  K steps are timed between barrier +
 synchronisation with HIP events on the launch stream.  The paged GQA decode
 workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
-same way and reported in "decode"; the long-context, varlen and chunked
-paged prefill workloads are reported in "extra".
+same way and reported in "decode"; the long-context, varlen, chunked paged
+prefill and FP8 prefill workloads are reported in "extra" (FP8 against the
+5.0 PFLOP/s dense fp8 peak).
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -30,11 +31,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "decode": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
     "chunked": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
+    "fp8": ["exact_io_aware_tile_amd/csrc/fa_fwd_fp8.hip"],
 }
 
 
@@ -48,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "copy"],
+    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -198,6 +201,23 @@ def run_paged_prefill(fa, case, steps, warmup, torch, np):
                          "traffic": measured_traffic("chunked")}}
 
 
+def run_fp8(fa, case, steps, warmup, torch, np):
+    q, k, v = (torch.from_numpy(case[n]).cuda() for n in ("q", "k", "v"))
+    o = torch.empty(case["q"].shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((case["batch"], case["hq"], case["nq"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fa_fwd_fp8(q, k, v, case["descale"], causal=case["causal"], out=o, lse=lse)
+
+    ms, wall_ms = time_steps(step, steps, warmup, torch)
+    flops = prefill_flops(case)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tf, "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": measured_traffic("fp8")}}
+
+
 def run_decode(fa, case, steps, warmup, torch, np):
     q = bf16_dev(case["q"], torch, np)
     kp = bf16_dev(case["k_pool"], torch, np)
@@ -276,6 +296,9 @@ def main():
         case = inputs.workload(6)
         out["chunked"] = (case, run_paged_prefill(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2),
                                                   torch, np))
+    if want("fp8", not args.no_extra):
+        case = inputs.workload(7)
+        out["fp8"] = (case, run_fp8(fa, case, args.steps, args.warmup, torch, np))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np))
@@ -314,7 +337,7 @@ def main():
                           "ms_per_step": round(dres["ms"], 4), "algorithmic_bytes": dres["bytes"],
                           "num_splits": dres["num_splits"], "roofline": dres["roofline"]}
     extra = []
-    for key in ("long", "varlen", "chunked"):
+    for key in ("long", "varlen", "chunked", "fp8"):
         if key in out:
             c, r = out[key]
             extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",

@@ -1,5 +1,6 @@
 // fa_device.h -- gfx950 device helpers: MFMA wrappers, bf16 packing,
-// base-2 transcendental wrappers and wave-level reductions.
+// base-2 transcendental wrappers, wave-level reductions, and the LDS-DMA,
+// wait and barrier primitives of the prefill pipelines.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,6 +51,49 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One LDS-DMA instruction: lane l's 16 bytes at base + off (base wave-uniform,
+// off a per-lane 32-bit byte offset) land at LDS byte address lds + 16 l
+// (lds wave-uniform).  Issued from asm so that the compiler does not track
+// the LDS write: it cannot tell the stage being filled from the stages being
+// read and would otherwise wait for every DMA in flight before the next LDS
+// read.  The kernel orders DMA and reads itself (wait_vmcnt + lds_barrier).
+// m0 is saved and restored around the instruction, with the one wait state
+// gfx9 needs between an m0 write and an LDS DMA.
+__device__ __forceinline__ void dma_16b(const void* base, uint32_t off, uint32_t lds) {
+  uint32_t m0_save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_save)
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt(N) with expcnt / lgkmcnt left open.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() carries a release
+// fence, which waits for every outstanding global load -- including the
+// LDS-DMA prefetches of later tiles -- and would drain the ring at each
+// phase.  Here each wave waits for exactly the DMA loads the next phase needs
+// (wait_vmcnt) before the barrier; LDS reads complete before their MFMA
+// consumers inside the phase, and the memory clobber keeps the compiler from
+// moving any LDS access across the barrier.
+// The scheduling fences on both sides keep each phase's instructions
+// (MFMA and exponentials included) inside the phase.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {

@@ -13,6 +13,8 @@ constexpr int kFwdRowsPerTileF32 = 128;
 // The bf16 prefill kernel addresses rows inside a 64-key tile with 32-bit
 // byte offsets: key/value row strides (elements) are limited to 2^24.
 constexpr int64_t kFwdMaxKvRowStrideBf16 = int64_t(1) << 24;
+// The FP8 prefill kernel: 256 query rows per workgroup, head_dim 128.
+constexpr int kFwdRowsPerTileFp8 = 256;
 // Paged prefill reads 16-token blocks.
 constexpr int kFwdPagedBlock = 16;
 
@@ -38,6 +40,8 @@ struct FwdParams {
   int32_t num_qtiles;    // query tiles per (sequence, head)
   int32_t causal;
   float scale_log2;      // scale * log2(e): scores are kept in base 2
+                         // (fp8: times the q and k descale factors)
+  float o_scale;         // fp8: the v descale factor, applied to O
   // Paged keys and values (chunked prefill, bf16): when `paged` is set,
   // q / o / lse are packed by cu_seqlens (the new queries of each sequence),
   // k / v point at the two pools, and key t of sequence s is token t % 16
@@ -76,6 +80,7 @@ struct DecodeParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
 // Parts for a requested num_splits (0: one per wave slot of the current

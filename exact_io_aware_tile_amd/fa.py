@@ -7,6 +7,7 @@ is raised.
 
 Layouts (see include/fa.h):
     fa_fwd:          q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o like q, lse [B, Hq, Nq]
+    fa_fwd_fp8:      as fa_fwd with uint8 E4M3 q/k/v and per-tensor descale factors -> o bf16
     fa_fwd_varlen:   q [T, Hq, d], k/v [T, Hkv, d], cu_seqlens int32 [S+1] -> o, lse [Hq, T]
     fa_fwd_paged:    q [Tq, Hq, d] (chunks packed by cu_seqlens_q int32 [S+1]), pools and
                      block_table as for decode, seq_lens_k int32 [S] -> o like q, lse [Hq, Tq]
@@ -38,6 +39,15 @@ class FwdArgs(ctypes.Structure):
                 ("dtype", ctypes.c_int), ("scale", _F), ("causal", _I32)]
 
 
+class FwdFp8Args(ctypes.Structure):
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o", _P), ("lse", _P),
+                ("batch", _I32), ("seqlen_q", _I32), ("seqlen_k", _I32), ("heads_q", _I32),
+                ("heads_kv", _I32), ("head_dim", _I32),
+                ("q_stride", _I64 * 3), ("k_stride", _I64 * 3), ("v_stride", _I64 * 3),
+                ("o_stride", _I64 * 3),
+                ("q_descale", _F), ("k_descale", _F), ("v_descale", _F), ("scale", _F), ("causal", _I32)]
+
+
 class FwdVarlenArgs(ctypes.Structure):
     _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o", _P), ("lse", _P), ("cu_seqlens", _P),
                 ("num_seqs", _I32), ("total_tokens", _I32), ("max_seqlen", _I32), ("heads_q", _I32),
@@ -66,7 +76,7 @@ class FwdPagedArgs(ctypes.Structure):
                 ("max_blocks_per_seq", _I32), ("num_blocks", _I32), ("scale", _F), ("causal", _I32)]
 
 
-SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
+SYMBOLS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -88,6 +98,8 @@ def lib(path: str = LIB_PATH):
     L = ctypes.CDLL(path)
     L.fa_fwd.argtypes = [ctypes.POINTER(FwdArgs), _P]
     L.fa_fwd.restype = ctypes.c_int
+    L.fa_fwd_fp8.argtypes = [ctypes.POINTER(FwdFp8Args), _P]
+    L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), _P]
     L.fa_fwd_varlen.restype = ctypes.c_int
     L.fa_fwd_paged.argtypes = [ctypes.POINTER(FwdPagedArgs), _P]
@@ -170,6 +182,34 @@ def fa_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=Non
     a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     a.causal = int(bool(causal))
     _check(lib().fa_fwd(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_fp8(q, k, v, descale, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
+               return_lse: bool = True, stream=None):
+    """Dense attention over FP8 E4M3 codes (uint8 tensors q [B, Nq, Hq, d], k/v
+    [B, Nk, Hkv, d]) standing for descale[i] * value(code).  Returns (o, lse)
+    with o in bf16."""
+    torch = _torch()
+    _dev(q, k, v, out, lse)
+    for t in (q, k, v):
+        if t.dtype != torch.uint8:
+            raise TypeError("fa_fwd_fp8 takes E4M3 codes as uint8 tensors")
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if out is None:
+        out = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    a = FwdFp8Args()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = B, Nq, Nk, Hq, Hkv, d
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, name)[:] = list(t.stride()[:3])
+    a.q_descale, a.k_descale, a.v_descale = (float(x) for x in descale)
+    a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a.causal = int(bool(causal))
+    _check(lib().fa_fwd_fp8(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

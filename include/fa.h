@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_OK = 0,
@@ -96,6 +96,44 @@ typedef struct {
 } fa_fwd_args;
 
 fa_status fa_fwd(const fa_fwd_args *args, void *stream);
+
+/*
+ * fa_fwd_fp8 -- dense attention (MHA or GQA) over FP8 E4M3 inputs with
+ * per-tensor descale factors, the FP8 mode "S12 FlashAttention"
+ * (llminference.xinbetween.com), "Production notes / In production",
+ * credits to FlashAttention-3.
+ *
+ *   q  [batch, seqlen_q, heads_q,  head_dim] E4M3 codes (one byte each),
+ *      strides q_stride = {batch, seq, head}
+ *   k  [batch, seqlen_k, heads_kv, head_dim] E4M3, strides k_stride
+ *   v  [batch, seqlen_k, heads_kv, head_dim] E4M3, strides v_stride
+ *   o  [batch, seqlen_q, heads_q,  head_dim] bf16, strides o_stride (written)
+ *   lse [batch, heads_q, seqlen_q] fp32, contiguous (written; may be NULL)
+ *
+ * The inputs stand for q_descale * value(q), k_descale * value(k) and
+ * v_descale * value(v) (E4M3: sign, 4-bit exponent with bias 7, 3-bit
+ * mantissa, subnormals, no infinities); scores are scale * q . k over those
+ * tensors, with the causal and GQA conventions above.  Both products run on
+ * the FP8 matrix cores with fp32 accumulation; the softmax weights are
+ * rounded to E4M3 for the second product and O is normalised by the sum of
+ * the rounded weights, LSE by the fp32 sum.  head_dim 128; strides are in
+ * elements (bytes for the inputs) and multiples of 16 bytes; k and v
+ * sequence strides at most 2^24.  Descale factors must be positive and
+ * finite.  seqlen_q == 0 or batch == 0 is a no-op; seqlen_k == 0 writes
+ * O = 0 and LSE = -inf.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, head_dim;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  float q_descale, k_descale, v_descale;
+  float scale;
+  int32_t causal;
+} fa_fwd_fp8_args;
+
+fa_status fa_fwd_fp8(const fa_fwd_fp8_args *args, void *stream);
 
 /*
  * fa_fwd_varlen -- packed variable-length sequences, no padding tokens.

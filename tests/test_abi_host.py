@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 3
+    assert L.fa_abi_version() == declared == 4
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -66,6 +66,7 @@ STRUCTS = {
     "fa_fwd_args": fa.FwdArgs,
     "fa_fwd_varlen_args": fa.FwdVarlenArgs,
     "fa_fwd_paged_args": fa.FwdPagedArgs,
+    "fa_fwd_fp8_args": fa.FwdFp8Args,
     "fa_decode_paged_args": fa.DecodePagedArgs,
 }
 
@@ -135,6 +136,48 @@ def test_fwd_empty_is_noop(L):
         assert L.fa_fwd(ctypes.byref(a), None) == fa.FA_OK
         assert L.fa_last_error() == b""
     assert L.fa_fwd(None, None) == fa.FA_ERR_NULL_POINTER
+
+
+def fp8_args(**kw):
+    a = fa.FwdFp8Args()
+    a.batch, a.seqlen_q, a.seqlen_k, a.heads_q, a.heads_kv, a.head_dim = 1, 8, 8, 2, 2, 128
+    a.q_descale = a.k_descale = a.v_descale = 0.01
+    a.scale, a.causal = 0.088, 1
+    a.q = a.k = a.v = a.o = 0x1000
+    for arr in (a.q_stride, a.k_stride, a.v_stride):
+        arr[:] = [8 * 2 * 128, 2 * 128, 128]
+    a.o_stride[:] = [8 * 2 * 128, 2 * 128, 128]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(q_descale=0.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(v_descale=float("inf")), fa.FA_ERR_BAD_SHAPE),
+    (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(k=None), fa.FA_ERR_NULL_POINTER),
+    (dict(q_stride=[2048, 264, 8]), fa.FA_ERR_BAD_SHAPE),   # 8-byte q stride
+    (dict(o_stride=[2048, 260, 128]), fa.FA_ERR_BAD_SHAPE),
+    (dict(v=0x1008), fa.FA_ERR_BAD_SHAPE),
+    (dict(k_stride=[1 << 30, (1 << 24) + 16, 128]), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fp8_rejects_before_launch(L, kw, status):
+    a = fp8_args(**kw)
+    assert L.fa_fwd_fp8(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_fp8_empty_is_noop(L):
+    for kw in (dict(batch=0), dict(seqlen_q=0)):
+        a = fp8_args(q=None, k=None, v=None, o=None, **kw)
+        assert L.fa_fwd_fp8(ctypes.byref(a), None) == fa.FA_OK
 
 
 def varlen_args(**kw):

@@ -456,3 +456,99 @@ def test_paged_prefill_workload_sampled(gpu):
     rows = np.array(sorted(rows), dtype=np.int64)
     og, lg, o_ref, lse_ref = run_paged_prefill(gpu, case, True, rows=rows)
     check(og, lg, o_ref, lse_ref, "bf16", "paged prefill workload sampled rows")
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 prefill
+# --------------------------------------------------------------------------
+# Tolerance of the FP8 path against the fp64 oracle on the same descaled
+# inputs.  Scores and LSE are computed in fp32 from exact FP8 products: LSE
+# keeps LSE_TOL.  O differs by the E4M3 rounding of the weights fed to P.V
+# (relative error up to 2^-4 per weight; O is normalised by the sum of the
+# rounded weights, so it stays a convex combination of V rows and the error
+# scales with the spread of the V rows that carry weight: largest for rows
+# with two or three comparable keys, about 2^-5 * |v_i - v_j|) plus bf16
+# output rounding (2^-9 relative).  With unit-variance V: max |dO| <= 0.08,
+# mean |dO| <= 0.006.
+FP8_TOL = (0.08, 0.006)
+
+
+def run_fp8(fa, case, causal, rows=None):
+    q, k, v = (torch.from_numpy(case[n]).cuda() for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd_fp8(q, k, v, case["descale"], causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fp8_dense(case["q"], case["k"], case["v"], case["descale"], causal=causal, rows=rows)
+    og = host(o).transpose(0, 2, 1, 3)
+    lg = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        og = og.reshape(-1, og.shape[-1])[rows]
+        lg = lg.reshape(-1)[rows]
+    return og, lg, o_ref, lse_ref
+
+
+def check_fp8(og, lg, o_ref, lse_ref, what):
+    tmax, tmean = FP8_TOL
+    err = np.abs(og - o_ref)
+    assert np.isfinite(og).all(), f"{what}: non-finite output"
+    assert err.max() <= tmax, f"{what}: max |dO| = {err.max():.3e} > {tmax}"
+    assert err.mean() <= tmean, f"{what}: mean |dO| = {err.mean():.3e} > {tmean}"
+    fin = np.isfinite(lse_ref)
+    np.testing.assert_array_equal(np.isfinite(lg), fin, err_msg=f"{what}: LSE finiteness")
+    np.testing.assert_array_equal(lg[~fin], lse_ref[~fin])
+    if fin.any():
+        e = np.abs(lg[fin] - lse_ref[fin]).max()
+        assert e <= LSE_TOL, f"{what}: max |dLSE| = {e:.3e}"
+
+
+FP8_SHAPES = [
+    # B, Nq, Nk, Hq, Hkv
+    (1, 1, 1, 1, 1),
+    (1, 64, 64, 1, 1),
+    (1, 300, 300, 2, 2),
+    (2, 513, 513, 4, 2),
+    (2, 100, 260, 2, 1),   # more keys than queries (end-aligned causal)
+    (1, 300, 77, 2, 2),    # more queries than keys: early causal rows see no key
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", FP8_SHAPES)
+def test_fp8_parity(gpu, shape, causal):
+    B, Nq, Nk, Hq, Hkv = shape
+    case = inputs.fp8_case(810 + Nq + Nk, B, Nq, Nk, Hq, Hkv, 128)
+    og, lg, o_ref, lse_ref = run_fp8(gpu, case, causal)
+    check_fp8(og.reshape(-1, 128), lg.reshape(-1), o_ref.reshape(-1, 128), lse_ref.reshape(-1),
+              f"fp8 {shape} causal={causal}")
+
+
+def test_fp8_single_key_returns_that_value(gpu):
+    # one visible key: its weight is 1 (exact in E4M3), so O = v_descale * v
+    # up to the bf16 rounding of the output
+    case = inputs.fp8_case(830, 2, 40, 40, 2, 2, 128)
+    og, lg, o_ref, lse_ref = run_fp8(gpu, case, True)
+    v = inputs.e4m3_to_f32(case["v"]).astype(np.float64) * float(case["descale"][2])
+    first = og[:, :, 0, :]          # [B, Hq, d]: row 0 sees key 0 only
+    np.testing.assert_allclose(first, v[:, 0, :, :], rtol=2.0 ** -8, atol=0)
+
+
+def test_fp8_empty_keys(gpu):
+    case = inputs.fp8_case(831, 1, 20, 1, 2, 2, 128)
+    q = torch.from_numpy(case["q"]).cuda()
+    kv = torch.empty((1, 0, 2, 128), dtype=torch.uint8, device="cuda")
+    o, lse = gpu.fa_fwd_fp8(q, kv, kv, case["descale"], causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert torch.all(torch.isneginf(lse))
+
+
+def test_fp8_workload_sampled(gpu):
+    case = inputs.workload(7)
+    B, N, H = case["batch"], case["nq"], case["hq"]
+    rng = np.random.default_rng(7)
+    rows = set(rng.integers(0, B * H * N, size=384).tolist())
+    for b in range(B):  # tile edges and the last row of some heads
+        for i in (0, 1, 255, 256, 1023, N - 1):
+            rows.add((b * H + int(rng.integers(0, H))) * N + i)
+    rows = np.array(sorted(rows), dtype=np.int64)
+    og, lg, o_ref, lse_ref = run_fp8(gpu, case, True, rows=rows)
+    check_fp8(og, lg, o_ref, lse_ref, "fp8 workload sampled rows")
