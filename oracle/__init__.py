@@ -46,6 +46,7 @@ def _load(path: str = _LIB):
         build(out=path)
     lib = ctypes.CDLL(path)
     P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    U64, U32 = ctypes.c_uint64, ctypes.c_uint32
     lib.oracle_attn_dense.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, I, D, P, I64, P, P, I]
     lib.oracle_attn_varlen.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P, I, D, P, I64, P, P, I]
     lib.oracle_attn_decode_paged.argtypes = [P, P, P, I, P, P, P, I, P, I, I, I, I, I, I, D, P,
@@ -53,6 +54,12 @@ def _load(path: str = _LIB):
     lib.oracle_attn_paged_prefill.argtypes = [P, P, P, I, P, I, P, P, P, I, P, I, I, I, I, I, I, D,
                                               P, I64, P, P, I]
     lib.oracle_max_threads.argtypes = [I]
+    lib.oracle_attn_dense_dropout.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, I, D, I, U64, U32, P,
+                                              I64, P, P, I]
+    lib.oracle_attn_varlen_dropout.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P, I, D, I, U64, U32, P,
+                                               I64, P, P, I]
+    lib.oracle_philox4x32_10.argtypes = [P, P, P]
+    lib.oracle_philox4x32_10.restype = None
     lib.oracle_decode_e4m3.argtypes = [P, P, I64]
     lib.oracle_decode_e4m3.restype = None
     for f in (lib.oracle_attn_dense, lib.oracle_attn_varlen, lib.oracle_attn_decode_paged,
@@ -255,3 +262,76 @@ def fp8_dense(q8, k8, v8, descale, *, causal: bool, scale: float | None = None, 
     k = decode_e4m3(k8, lib=lib) * kd
     v = decode_e4m3(v8, lib=lib) * vd
     return dense(q, k, v, causal=causal, scale=scale, rows=rows, nthreads=nthreads, lib=lib)
+
+
+def dropout_threshold(p: float) -> int:
+    """Byte threshold t of a dropout probability: t = rint(256 p), p in [0, 1)
+    with t <= 255; a weight is kept iff its random byte >= t, with probability
+    (256 - t) / 256, and kept weights are scaled by 256 / (256 - t)."""
+    t = int(np.rint(float(p) * 256.0))
+    if not (0.0 <= float(p) < 1.0) or t > 255:
+        raise ValueError("dropout probability must be in [0, 255.5/256)")
+    return t
+
+
+def philox4x32_10(ctr, key, *, lib=None):
+    """One Philox-4x32-10 block: 4 uint32 counter words, 2 key words -> 4 words."""
+    L = lib or _load()
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    L.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def dense_dropout(q, k, v, *, causal: bool, dropout_p: float, seed: int, offset: int = 0,
+                  scale: float | None = None, rows=None, nthreads: int = 0, lib=None):
+    """``dense`` with dropout of the normalised weights: the weight of row
+    (b, h, i) on key j is kept iff byte j % 16 of Philox-4x32-10(counter {j /
+    16, row, row >> 32, offset}, key {seed, seed >> 32}) is >= the threshold
+    of ``dropout_threshold``, row = (b * Hq + h) * Nq + i."""
+    L = lib or _load()
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    t = dropout_threshold(dropout_p)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r, nr = _rows(rows)
+    n = nr if r is not None else B * Hq * Nq
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    qs, ks, vs = _strides(q, 3), _strides(k, 3), _strides(v, 3)
+    st = L.oracle_attn_dense_dropout(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Nq, Nk, Hq, Hkv, d,
+                                     _ptr(qs), _ptr(ks), _ptr(vs), int(bool(causal)), scale, t,
+                                     int(seed) & (2**64 - 1), int(offset) & (2**32 - 1), _ptr(r), nr,
+                                     _ptr(o), _ptr(lse), int(nthreads))
+    if st:
+        raise ValueError(f"oracle_attn_dense_dropout failed with status {st}")
+    if r is None:
+        return o.reshape(B, Hq, Nq, d), lse.reshape(B, Hq, Nq)
+    return o, lse
+
+
+def varlen_dropout(q, k, v, cu_seqlens, *, causal: bool, dropout_p: float, seed: int, offset: int = 0,
+                   scale: float | None = None, rows=None, nthreads: int = 0, lib=None):
+    """``varlen`` with dropout; the row of (h, token t) is h * T + t and keys
+    are numbered within their sequence."""
+    L = lib or _load()
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    t = dropout_threshold(dropout_p)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r, nr = _rows(rows)
+    n = nr if r is not None else Hq * T
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    qs, ks, vs = _strides(q, 2), _strides(k, 2), _strides(v, 2)
+    st = L.oracle_attn_varlen_dropout(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(cu), len(cu) - 1,
+                                      Hq, Hkv, d, _ptr(qs), _ptr(ks), _ptr(vs), int(bool(causal)), scale,
+                                      t, int(seed) & (2**64 - 1), int(offset) & (2**32 - 1), _ptr(r), nr,
+                                      _ptr(o), _ptr(lse), int(nthreads))
+    if st:
+        raise ValueError(f"oracle_attn_varlen_dropout failed with status {st}")
+    if r is None:
+        return o.reshape(Hq, T, d), lse.reshape(Hq, T)
+    return o, lse

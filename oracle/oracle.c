@@ -34,6 +34,10 @@
  *     logical key t of sequence b is pool[block_table[b][t / block]][g][t % block]
  *     with g = h / (Hq / Hkv), for t < seq_len[b].
  *
+ * Dropout of the normalised weights (the *_dropout entry points) is described
+ * at dropout_t below; the generator it draws from is Philox-4x32-10, written
+ * from its published definition and pinned to the published known answers.
+ *
  * Status codes: 0 ok, 1 bad argument, 2 out of memory.
  */
 #include <math.h>
@@ -57,6 +61,66 @@ static double load(const void *p, int dtype, int64_t i) {
 }
 
 /*
+ * Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011): ten rounds on a 4-word counter under a 2-word
+ * key.  A round multiplies counter words 0 and 2 by M0 and M1 into 64-bit
+ * products and forms {hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0}; between rounds
+ * the key words advance by W0 and W1.
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  out[0] = c0, out[1] = c1, out[2] = c2, out[3] = c3;
+}
+
+/*
+ * Attention dropout ("FlashAttention: The Algorithm That Beat the Memory
+ * Wall", repo-explainer.com, "How the Repo Connects Python to Bare-Metal
+ * CUDA" and "Why Templates Matter Here" name dropout among the kernel's
+ * parameters and specialisations; what it computes is the usual reading):
+ * each normalised weight of row `row` and key j is kept with probability
+ * (256 - t) / 256 and scaled by 256 / (256 - t), else zeroed; the LSE is
+ * that of the weights before dropout.  The keep decision for (row, j) is
+ * byte j % 16 (little-endian) of the Philox-4x32-10 output for counter
+ * {j / 16, row low word, row high word, offset} and key {seed low, seed
+ * high}: keep iff that byte >= t.
+ */
+typedef struct {
+  int threshold; /* t in [0, 255]; 0 keeps everything */
+  uint64_t seed;
+  uint32_t offset;
+  int64_t row; /* the row's id (its index in the LSE layout) */
+} dropout_t;
+
+static int dropout_keep(const dropout_t *dp, int64_t j) {
+  const uint32_t ctr[4] = {(uint32_t)(j / 16), (uint32_t)dp->row, (uint32_t)((uint64_t)dp->row >> 32),
+                           dp->offset};
+  const uint32_t key[2] = {(uint32_t)dp->seed, (uint32_t)(dp->seed >> 32)};
+  uint32_t out[4];
+  oracle_philox4x32_10(ctr, key, out);
+  const uint32_t byte = (out[(j % 16) / 4] >> (8 * (j % 4))) & 0xFFu;
+  return (int)byte >= dp->threshold;
+}
+
+static void attend_row_dropout(const void *q, const void *k, const void *v, int dtype, int d,
+                               double scale, int64_t qoff, const int64_t *koff,
+                               const int64_t *voff, int64_t n, double *s, double *o,
+                               double *lse, const dropout_t *dp);
+
+/*
  * One query row against an explicit list of key/value row offsets.
  *   qoff        : element offset of the query row in q
  *   koff[j]     : element offset of key row j in k, voff[j] likewise in v
@@ -68,6 +132,14 @@ static void attend_row(const void *q, const void *k, const void *v, int dtype, i
                        double scale, int64_t qoff, const int64_t *koff,
                        const int64_t *voff, int64_t n, double *s, double *o,
                        double *lse) {
+  attend_row_dropout(q, k, v, dtype, d, scale, qoff, koff, voff, n, s, o, lse, NULL);
+}
+
+/* attend_row with optional dropout of the normalised weights (dp may be NULL). */
+static void attend_row_dropout(const void *q, const void *k, const void *v, int dtype, int d,
+                               double scale, int64_t qoff, const int64_t *koff,
+                               const int64_t *voff, int64_t n, double *s, double *o,
+                               double *lse, const dropout_t *dp) {
   for (int c = 0; c < d; ++c) o[c] = 0.0;
   if (n <= 0) {
     *lse = -INFINITY;
@@ -89,9 +161,13 @@ static void attend_row(const void *q, const void *k, const void *v, int dtype, i
     s[j] = exp(s[j] - m);
     z += s[j];
   }
-  /* Weighted sum of values, then normalise. */
-  for (int64_t j = 0; j < n; ++j)
-    for (int c = 0; c < d; ++c) o[c] += s[j] * load(v, dtype, voff[j] + c);
+  /* Weighted sum of values (dropout: kept weights rescaled, dropped ones
+   * zero), then normalise by the full sum. */
+  const double keep_scale = dp ? 256.0 / (256 - dp->threshold) : 1.0;
+  for (int64_t j = 0; j < n; ++j) {
+    const double w = dp ? (dropout_keep(dp, j) ? s[j] * keep_scale : 0.0) : s[j];
+    for (int c = 0; c < d; ++c) o[c] += w * load(v, dtype, voff[j] + c);
+  }
   for (int c = 0; c < d; ++c) o[c] /= z;
   *lse = m + log(z);
 }
@@ -138,11 +214,37 @@ void oracle_decode_e4m3(const uint8_t *src, double *dst, int64_t n) {
  * Rows are flattened ids r = (b * Hq + h) * Nq + i; rows == NULL means all
  * B*Hq*Nq rows in that order.  o is [nrows, d], lse is [nrows].
  */
+static int dense_impl(const void *q, const void *k, const void *v, int dtype, int B, int Nq, int Nk,
+                      int Hq, int Hkv, int d, const int64_t *qs, const int64_t *ks, const int64_t *vs,
+                      int causal, double scale, const int64_t *rows, int64_t nrows, double *o,
+                      double *lse, int nthreads, const dropout_t *drop);
+
 int oracle_attn_dense(const void *q, const void *k, const void *v, int dtype, int B,
                       int Nq, int Nk, int Hq, int Hkv, int d, const int64_t *qs,
                       const int64_t *ks, const int64_t *vs, int causal, double scale,
                       const int64_t *rows, int64_t nrows, double *o, double *lse,
                       int nthreads) {
+  return dense_impl(q, k, v, dtype, B, Nq, Nk, Hq, Hkv, d, qs, ks, vs, causal, scale, rows, nrows, o,
+                    lse, nthreads, NULL);
+}
+
+/* Dense attention with dropout of the normalised weights (see dropout_t);
+ * the row id of (b, h, i) is (b * Hq + h) * Nq + i. */
+int oracle_attn_dense_dropout(const void *q, const void *k, const void *v, int dtype, int B,
+                              int Nq, int Nk, int Hq, int Hkv, int d, const int64_t *qs,
+                              const int64_t *ks, const int64_t *vs, int causal, double scale,
+                              int threshold, uint64_t seed, uint32_t offset, const int64_t *rows,
+                              int64_t nrows, double *o, double *lse, int nthreads) {
+  if (threshold < 0 || threshold > 255) return 1;
+  dropout_t drop = {threshold, seed, offset, 0};
+  return dense_impl(q, k, v, dtype, B, Nq, Nk, Hq, Hkv, d, qs, ks, vs, causal, scale, rows, nrows, o,
+                    lse, nthreads, &drop);
+}
+
+static int dense_impl(const void *q, const void *k, const void *v, int dtype, int B, int Nq, int Nk,
+                      int Hq, int Hkv, int d, const int64_t *qs, const int64_t *ks, const int64_t *vs,
+                      int causal, double scale, const int64_t *rows, int64_t nrows, double *o,
+                      double *lse, int nthreads, const dropout_t *drop) {
   if (!q || !k || !v || !o || !lse || !qs || !ks || !vs) return 1;
   if (B < 0 || Nq < 0 || Nk < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return 1;
   if (!rows) nrows = (int64_t)B * Hq * Nq;
@@ -177,8 +279,13 @@ int oracle_attn_dense(const void *q, const void *k, const void *v, int dtype, in
           koff[j] = b * ks[0] + j * ks[1] + g * ks[2];
           voff[j] = b * vs[0] + j * vs[1] + g * vs[2];
         }
-        attend_row(q, k, v, dtype, d, scale, b * qs[0] + i * qs[1] + h * qs[2], koff, voff,
-                   n, s, o + r * d, lse + r);
+        dropout_t dp;
+        if (drop) {
+          dp = *drop;
+          dp.row = id; /* (b * Hq + h) * Nq + i */
+        }
+        attend_row_dropout(q, k, v, dtype, d, scale, b * qs[0] + i * qs[1] + h * qs[2], koff, voff,
+                           n, s, o + r * d, lse + r, drop ? &dp : NULL);
       }
     }
     free(s);
@@ -194,11 +301,38 @@ int oracle_attn_dense(const void *q, const void *k, const void *v, int dtype, in
  * [cu[s], cu[s+1]).  Rows are flattened ids r = h * T + t (rows == NULL:
  * all Hq*T).  Keys are the query's own sequence, causal in local positions.
  */
+static int varlen_impl(const void *q, const void *k, const void *v, int dtype, const int32_t *cu,
+                       int nseq, int Hq, int Hkv, int d, const int64_t *qs, const int64_t *ks,
+                       const int64_t *vs, int causal, double scale, const int64_t *rows,
+                       int64_t nrows, double *o, double *lse, int nthreads, const dropout_t *drop);
+
 int oracle_attn_varlen(const void *q, const void *k, const void *v, int dtype,
                        const int32_t *cu, int nseq, int Hq, int Hkv, int d,
                        const int64_t *qs, const int64_t *ks, const int64_t *vs, int causal,
                        double scale, const int64_t *rows, int64_t nrows, double *o,
                        double *lse, int nthreads) {
+  return varlen_impl(q, k, v, dtype, cu, nseq, Hq, Hkv, d, qs, ks, vs, causal, scale, rows, nrows, o,
+                     lse, nthreads, NULL);
+}
+
+/* Packed attention with dropout (see dropout_t); the row id of (h, token t)
+ * is h * T + t, keys are numbered within their sequence. */
+int oracle_attn_varlen_dropout(const void *q, const void *k, const void *v, int dtype,
+                               const int32_t *cu, int nseq, int Hq, int Hkv, int d,
+                               const int64_t *qs, const int64_t *ks, const int64_t *vs, int causal,
+                               double scale, int threshold, uint64_t seed, uint32_t offset,
+                               const int64_t *rows, int64_t nrows, double *o, double *lse,
+                               int nthreads) {
+  if (threshold < 0 || threshold > 255) return 1;
+  dropout_t drop = {threshold, seed, offset, 0};
+  return varlen_impl(q, k, v, dtype, cu, nseq, Hq, Hkv, d, qs, ks, vs, causal, scale, rows, nrows, o,
+                     lse, nthreads, &drop);
+}
+
+static int varlen_impl(const void *q, const void *k, const void *v, int dtype, const int32_t *cu,
+                       int nseq, int Hq, int Hkv, int d, const int64_t *qs, const int64_t *ks,
+                       const int64_t *vs, int causal, double scale, const int64_t *rows,
+                       int64_t nrows, double *o, double *lse, int nthreads, const dropout_t *drop) {
   if (!q || !k || !v || !cu || !o || !lse || !qs || !ks || !vs) return 1;
   if (nseq < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) return 1;
   if (cu[0] != 0) return 1;
@@ -240,8 +374,13 @@ int oracle_attn_varlen(const void *q, const void *k, const void *v, int dtype,
           koff[j] = (start + j) * ks[0] + g * ks[1];
           voff[j] = (start + j) * vs[0] + g * vs[1];
         }
-        attend_row(q, k, v, dtype, d, scale, t * qs[0] + h * qs[1], koff, voff, n, s,
-                   o + r * d, lse + r);
+        dropout_t dp;
+        if (drop) {
+          dp = *drop;
+          dp.row = id; /* h * T + t */
+        }
+        attend_row_dropout(q, k, v, dtype, d, scale, t * qs[0] + h * qs[1], koff, voff, n, s,
+                           o + r * d, lse + r, drop ? &dp : NULL);
       }
     }
     free(s);

@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_dropout as DR
 from tests import test_oracle_fp8 as F
 from tests import test_oracle_paged_prefill as C
 from tests import test_oracle_pins as P
@@ -32,8 +33,8 @@ MUTANTS = {
                                 "int64_t last = causal ? i :"),
     "interleaved kv groups": ("        int64_t g = h / group;\n        int64_t last",
                               "        int64_t g = h % Hkv;\n        int64_t last"),
-    "values reversed": ("o[c] += s[j] * load(v, dtype, voff[j] + c);",
-                        "o[c] += s[j] * load(v, dtype, voff[n - 1 - j] + c);"),
+    "values reversed": ("o[c] += w * load(v, dtype, voff[j] + c);",
+                        "o[c] += w * load(v, dtype, voff[n - 1 - j] + c);"),
     "key row reversed": ("load(k, dtype, koff[j] + c);", "load(k, dtype, koff[j] + (d - 1 - c));"),
     "bf16 widening": ("uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;",
                       "uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 15;"),
@@ -54,6 +55,19 @@ MUTANTS = {
     "e4m3 subnormal scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     "e4m3 implicit bit dropped": ("v = ldexp(8.0 + m, e - 10);", "v = ldexp((double)m, e - 10);"),
     "e4m3 sign ignored": ("dst[i] = sign ? -v : v;", "dst[i] = v;"),
+    "philox key not advanced": ("k0 += W0;", "(void)W0;"),
+    "philox products swapped": ("c0 = hi1 ^ c1 ^ k0;", "c0 = hi0 ^ c1 ^ k0;"),
+    "philox multipliers swapped": ("p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;",
+                                   "p0 = (uint64_t)M1 * c0, p1 = (uint64_t)M0 * c2;"),
+    "dropout big-endian byte": ("(out[(j % 16) / 4] >> (8 * (j % 4)))",
+                                "(out[(j % 16) / 4] >> (8 * (3 - j % 4)))"),
+    "dropout strict threshold": ("return (int)byte >= dp->threshold;", "return (int)byte > dp->threshold;"),
+    "dropout scale missing": ("dp ? 256.0 / (256 - dp->threshold) : 1.0", "1.0"),
+    "dropout counter word": ("{(uint32_t)(j / 16), (uint32_t)dp->row", "{(uint32_t)(j % 16), (uint32_t)dp->row"),
+    "dropout offset ignored": ("(uint32_t)((uint64_t)dp->row >> 32),\n                           dp->offset}",
+                               "(uint32_t)((uint64_t)dp->row >> 32),\n                           0u}"),
+    "dropout dense row layout": ("dp.row = id; /* (b * Hq + h) * Nq + i */", "dp.row = (h * B + b) * Nq + i;"),
+    "dropout packed row layout": ("dp.row = id; /* h * T + t */", "dp.row = t * Hq + h;"),
 }
 
 PINS = [
@@ -78,6 +92,12 @@ PINS = [
     (C.test_chunk_longer_than_context_starts_without_keys, {}),
     (F.test_decode_all_codes_match_torch, {}),
     (F.test_decode_closed_forms, {}),
+    (DR.test_philox_known_answers, {}),
+    (DR.test_keep_decisions_follow_the_counter_layout, {"p": 0.1}),
+    (DR.test_zero_probability_is_plain_and_lse_ignores_dropout, {}),
+    (DR.test_keep_rate_and_unbiased_scaling, {}),
+    (DR.test_single_packed_sequence_numbers_rows_like_dense, {}),
+    (DR.test_packed_keep_decisions_use_head_major_rows_and_local_keys, {}),
 ]
 
 
