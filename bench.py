@@ -9,8 +9,8 @@ already resident in HBM).  K steps are timed between barrier +
 synchronisation with HIP events on the launch stream.  The paged GQA decode
 workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
 same way and reported in "decode"; the long-context, varlen, chunked paged
-prefill and FP8 prefill workloads are reported in "extra" (FP8 against the
-5.0 PFLOP/s dense fp8 peak).
+prefill, FP8 prefill and dropout prefill workloads are reported in "extra"
+(FP8 against the 5.0 PFLOP/s dense fp8 peak).
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "decode": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
     "chunked": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "fp8": ["exact_io_aware_tile_amd/csrc/fa_fwd_fp8.hip"],
+    "dropout": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
 }
 
 
@@ -51,7 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "copy"],
+    ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "dropout",
+                                                 "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -141,8 +143,13 @@ def run_prefill(fa, case, steps, warmup, torch, np, kind):
     o = torch.empty_like(q)
     lse = torch.empty((case["batch"], case["hq"], case["nq"]), dtype=torch.float32, device="cuda")
 
-    def step():
-        fa.fa_fwd(q, k, v, causal=case["causal"], out=o, lse=lse)
+    if "dropout_p" in case:
+        def step():
+            fa.fa_fwd_dropout(q, k, v, dropout_p=case["dropout_p"], seed=case["seed"], offset=case["offset"],
+                              causal=case["causal"], out=o, lse=lse)
+    else:
+        def step():
+            fa.fa_fwd(q, k, v, causal=case["causal"], out=o, lse=lse)
 
     ms, wall_ms = time_steps(step, steps, warmup, torch)
     flops = prefill_flops(case)
@@ -299,6 +306,9 @@ def main():
     if want("fp8", not args.no_extra):
         case = inputs.workload(7)
         out["fp8"] = (case, run_fp8(fa, case, args.steps, args.warmup, torch, np))
+    if want("dropout", not args.no_extra):
+        case = inputs.workload(8)
+        out["dropout"] = (case, run_prefill(fa, case, args.steps, args.warmup, torch, np, "dropout"))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np))
@@ -337,7 +347,7 @@ def main():
                           "ms_per_step": round(dres["ms"], 4), "algorithmic_bytes": dres["bytes"],
                           "num_splits": dres["num_splits"], "roofline": dres["roofline"]}
     extra = []
-    for key in ("long", "varlen", "chunked", "fp8"):
+    for key in ("long", "varlen", "chunked", "fp8", "dropout"):
         if key in out:
             c, r = out[key]
             extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",

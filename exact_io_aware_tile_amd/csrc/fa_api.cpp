@@ -86,41 +86,60 @@ int decode_parts(const fa_decode_paged_args* a) {
   return fa::decode_num_parts(a->num_splits, a->batch, a->heads_q, a->heads_q / a->heads_kv, a->max_seq_len);
 }
 
-}  // namespace
 
-FA_EXPORT fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
-  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd: args is NULL");
+// Dropout arguments -> byte threshold t = rint(256 p) (ties to even), seed
+// and offset in the parameter block; t == 0 leaves dropout off.
+fa_status set_dropout(const fa_dropout_args* d, fa_dtype dtype, const char* fn, fa::FwdParams& p) {
+  if (!d) return fail(FA_ERR_NULL_POINTER, "%s: dropout args is NULL", fn);
+  if (!(d->p >= 0.0) || !(d->p < 1.0))
+    return fail(FA_ERR_BAD_SHAPE, "%s: dropout probability must be in [0, 1)", fn);
+  const double t = std::nearbyint(256.0 * d->p);
+  if (t > 255.0) return fail(FA_ERR_BAD_SHAPE, "%s: dropout probability rounds to 256/256", fn);
+  if (t > 0.0 && dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: dropout is built for bf16", fn);
+  p.drop_t = (int32_t)t;
+  p.drop_seed_lo = (uint32_t)d->seed;
+  p.drop_seed_hi = (uint32_t)(d->seed >> 32);
+  p.drop_offset = d->offset;
+  p.drop_scale = (float)(256.0 / (256.0 - t));
+  return FA_OK;
+}
+
+fa_status fwd_dense(const fa_fwd_args* a, const fa_dropout_args* drop, const char* fn, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "%s: args is NULL", fn);
   if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: negative or zero size");
+    return fail(FA_ERR_BAD_SHAPE, "%s: negative or zero size", fn);
   if (a->heads_q % a->heads_kv)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
+    return fail(FA_ERR_BAD_SHAPE, "%s: heads_q (%d) is not a multiple of heads_kv (%d)", fn, a->heads_q,
                 a->heads_kv);
-  if (a->dtype != FA_F32 && a->dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: dtype %d", (int)a->dtype);
+  if (a->dtype != FA_F32 && a->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)a->dtype);
   if (a->head_dim != 64 && a->head_dim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: head_dim %d, supported 64 and 128", a->head_dim);
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported 64 and 128", fn, a->head_dim);
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: scale must be positive and finite");
+    return fail(FA_ERR_BAD_SHAPE, "%s: scale must be positive and finite", fn);
+  fa::FwdParams p{};
+  if (drop) {
+    const fa_status st = set_dropout(drop, a->dtype, fn, p);
+    if (st != FA_OK) return st;
+  }
   if (a->batch == 0 || a->seqlen_q == 0) return ok();
-  if (!a->q || !a->o) return fail(FA_ERR_NULL_POINTER, "fa_fwd: q and o are required");
+  if (!a->q || !a->o) return fail(FA_ERR_NULL_POINTER, "%s: q and o are required", fn);
   if (a->seqlen_k > 0 && (!a->k || !a->v))
-    return fail(FA_ERR_NULL_POINTER, "fa_fwd: k and v are required when seqlen_k > 0");
+    return fail(FA_ERR_NULL_POINTER, "%s: k and v are required when seqlen_k > 0", fn);
   const int64_t e16 = a->dtype == FA_BF16 ? 8 : 4;
   if (!strides_ok(a->q_stride, 3, e16) || !strides_ok(a->k_stride, 3, e16) || !strides_ok(a->v_stride, 3, e16) ||
       !strides_ok(a->o_stride, 3, e16))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: strides must be non-negative multiples of %lld elements",
+    return fail(FA_ERR_BAD_SHAPE, "%s: strides must be non-negative multiples of %lld elements", fn,
                 (long long)e16);
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd: q, k, v, o must be 16-byte aligned");
+    return fail(FA_ERR_BAD_SHAPE, "%s: q, k, v, o must be 16-byte aligned", fn);
   if (a->dtype == FA_BF16 &&
       (a->k_stride[1] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[1] > fa::kFwdMaxKvRowStrideBf16))
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd: bf16 k/v row strides above %lld elements",
+    return fail(FA_ERR_UNSUPPORTED, "%s: bf16 k/v row strides above %lld elements", fn,
                 (long long)fa::kFwdMaxKvRowStrideBf16);
   const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
   const int64_t qtiles = (a->seqlen_q + rows - 1) / rows;
-  if (qtiles * a->heads_q * a->batch > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "fa_fwd: grid too large");
+  if (qtiles * a->heads_q * a->batch > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
 
-  fa::FwdParams p{};
   p.q = a->q;
   p.k = a->k;
   p.v = a->v;
@@ -143,8 +162,87 @@ FA_EXPORT fa_status fa_fwd(const fa_fwd_args* a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = a->dtype == FA_BF16 ? fa::launch_fwd_bf16(p, a->head_dim, s)
                                            : fa::launch_fwd_f32(p, a->head_dim, s);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+fa_status fwd_varlen(const fa_fwd_varlen_args* a, const fa_dropout_args* drop, const char* fn, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "%s: args is NULL", fn);
+  if (a->num_seqs < 0 || a->total_tokens < 0 || a->max_seqlen < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
+    return fail(FA_ERR_BAD_SHAPE, "%s: negative or zero size", fn);
+  if (a->heads_q % a->heads_kv)
+    return fail(FA_ERR_BAD_SHAPE, "%s: heads_q (%d) is not a multiple of heads_kv (%d)", fn, a->heads_q,
+                a->heads_kv);
+  if (a->dtype != FA_F32 && a->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported 64 and 128", fn, a->head_dim);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(FA_ERR_BAD_SHAPE, "%s: scale must be positive and finite", fn);
+  fa::FwdParams p{};
+  if (drop) {
+    const fa_status st = set_dropout(drop, a->dtype, fn, p);
+    if (st != FA_OK) return st;
+  }
+  if (a->num_seqs == 0 || a->max_seqlen == 0 || a->total_tokens == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->o || !a->cu_seqlens)
+    return fail(FA_ERR_NULL_POINTER, "%s: q, k, v, o and cu_seqlens are required", fn);
+  const int64_t e16 = a->dtype == FA_BF16 ? 8 : 4;
+  if (!strides_ok(a->q_stride, 2, e16) || !strides_ok(a->k_stride, 2, e16) || !strides_ok(a->v_stride, 2, e16) ||
+      !strides_ok(a->o_stride, 2, e16))
+    return fail(FA_ERR_BAD_SHAPE, "%s: strides must be non-negative multiples of %lld elements", fn,
+                (long long)e16);
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(FA_ERR_BAD_SHAPE, "%s: q, k, v, o must be 16-byte aligned", fn);
+  if (a->dtype == FA_BF16 &&
+      (a->k_stride[0] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[0] > fa::kFwdMaxKvRowStrideBf16))
+    return fail(FA_ERR_UNSUPPORTED, "%s: bf16 k/v token strides above %lld elements", fn,
+                (long long)fa::kFwdMaxKvRowStrideBf16);
+  const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
+  const int64_t qtiles = (a->max_seqlen + rows - 1) / rows;
+  if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_seqlens = a->cu_seqlens;
+  p.q_bs = 0, p.q_ss = a->q_stride[0], p.q_hs = a->q_stride[1];
+  p.k_bs = 0, p.k_ss = a->k_stride[0], p.k_hs = a->k_stride[1];
+  p.v_bs = 0, p.v_ss = a->v_stride[0], p.v_hs = a->v_stride[1];
+  p.o_bs = 0, p.o_ss = a->o_stride[0], p.o_hs = a->o_stride[1];
+  p.batch = a->num_seqs;
+  p.seqlen_q = a->max_seqlen;
+  p.seqlen_k = a->max_seqlen;
+  p.total_tokens = a->total_tokens;
+  p.heads_q = a->heads_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.num_qtiles = (int32_t)qtiles;
+  p.causal = a->causal ? 1 : 0;
+  p.scale_log2 = scale_log2(a->scale);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = a->dtype == FA_BF16 ? fa::launch_fwd_bf16(p, a->head_dim, s)
+                                           : fa::launch_fwd_f32(p, a->head_dim, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+FA_EXPORT fa_status fa_fwd(const fa_fwd_args* a, void* stream) { return fwd_dense(a, nullptr, "fa_fwd", stream); }
+
+FA_EXPORT fa_status fa_fwd_dropout(const fa_fwd_args* a, const fa_dropout_args* d, void* stream) {
+  if (!d) return fail(FA_ERR_NULL_POINTER, "fa_fwd_dropout: dropout args is NULL");
+  return fwd_dense(a, d, "fa_fwd_dropout", stream);
+}
+
+FA_EXPORT fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
+  return fwd_varlen(a, nullptr, "fa_fwd_varlen", stream);
+}
+
+FA_EXPORT fa_status fa_fwd_varlen_dropout(const fa_fwd_varlen_args* a, const fa_dropout_args* d, void* stream) {
+  if (!d) return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen_dropout: dropout args is NULL");
+  return fwd_varlen(a, d, "fa_fwd_varlen_dropout", stream);
 }
 
 FA_EXPORT fa_status fa_fwd_fp8(const fa_fwd_fp8_args* a, void* stream) {
@@ -198,65 +296,6 @@ FA_EXPORT fa_status fa_fwd_fp8(const fa_fwd_fp8_args* a, void* stream) {
   p.o_scale = a->v_descale;
   const hipError_t e = fa::launch_fwd_fp8(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_fp8: launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
-
-FA_EXPORT fa_status fa_fwd_varlen(const fa_fwd_varlen_args* a, void* stream) {
-  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen: args is NULL");
-  if (a->num_seqs < 0 || a->total_tokens < 0 || a->max_seqlen < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: negative or zero size");
-  if (a->heads_q % a->heads_kv)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
-                a->heads_kv);
-  if (a->dtype != FA_F32 && a->dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: dtype %d", (int)a->dtype);
-  if (a->head_dim != 64 && a->head_dim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: head_dim %d, supported 64 and 128", a->head_dim);
-  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: scale must be positive and finite");
-  if (a->num_seqs == 0 || a->max_seqlen == 0 || a->total_tokens == 0) return ok();
-  if (!a->q || !a->k || !a->v || !a->o || !a->cu_seqlens)
-    return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen: q, k, v, o and cu_seqlens are required");
-  const int64_t e16 = a->dtype == FA_BF16 ? 8 : 4;
-  if (!strides_ok(a->q_stride, 2, e16) || !strides_ok(a->k_stride, 2, e16) || !strides_ok(a->v_stride, 2, e16) ||
-      !strides_ok(a->o_stride, 2, e16))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: strides must be non-negative multiples of %lld elements",
-                (long long)e16);
-  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen: q, k, v, o must be 16-byte aligned");
-  if (a->dtype == FA_BF16 &&
-      (a->k_stride[0] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[0] > fa::kFwdMaxKvRowStrideBf16))
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: bf16 k/v token strides above %lld elements",
-                (long long)fa::kFwdMaxKvRowStrideBf16);
-  const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
-  const int64_t qtiles = (a->max_seqlen + rows - 1) / rows;
-  if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen: grid too large");
-
-  fa::FwdParams p{};
-  p.q = a->q;
-  p.k = a->k;
-  p.v = a->v;
-  p.o = a->o;
-  p.lse = a->lse;
-  p.cu_seqlens = a->cu_seqlens;
-  p.q_bs = 0, p.q_ss = a->q_stride[0], p.q_hs = a->q_stride[1];
-  p.k_bs = 0, p.k_ss = a->k_stride[0], p.k_hs = a->k_stride[1];
-  p.v_bs = 0, p.v_ss = a->v_stride[0], p.v_hs = a->v_stride[1];
-  p.o_bs = 0, p.o_ss = a->o_stride[0], p.o_hs = a->o_stride[1];
-  p.batch = a->num_seqs;
-  p.seqlen_q = a->max_seqlen;
-  p.seqlen_k = a->max_seqlen;
-  p.total_tokens = a->total_tokens;
-  p.heads_q = a->heads_q;
-  p.group = a->heads_q / a->heads_kv;
-  p.num_qtiles = (int32_t)qtiles;
-  p.causal = a->causal ? 1 : 0;
-  p.scale_log2 = scale_log2(a->scale);
-  hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = a->dtype == FA_BF16 ? fa::launch_fwd_bf16(p, a->head_dim, s)
-                                           : fa::launch_fwd_f32(p, a->head_dim, s);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_varlen: launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -1,6 +1,7 @@
 // fa_device.h -- gfx950 device helpers: MFMA wrappers, bf16 packing,
-// base-2 transcendental wrappers, wave-level reductions, and the LDS-DMA,
-// wait and barrier primitives of the prefill pipelines.
+// base-2 transcendental wrappers, wave-level reductions, the LDS-DMA,
+// wait and barrier primitives of the prefill pipelines, and the counter-based
+// generator and byte threshold of attention dropout.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -94,6 +95,44 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011), from its published definition: ten rounds on a
+// four-word counter; each round takes the 64-bit products of words 0 and 2
+// with the two round multipliers, and the new words are, in order, the high
+// half of the second product xor word 1 xor key word 0, its low half, the
+// high half of the first product xor word 3 xor key word 1, and its low
+// half.  The key words grow by the two Weyl constants after every round.
+// The key is wave-uniform, so its schedule stays in scalar registers; it is
+// rebuilt at each call (two scalar adds per round) instead of being hoisted
+// out of the caller's loop as twenty live registers.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+  asm volatile("" : "+s"(k0), "+s"(k1));
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// Keep mask of two dropout bytes for two bf16 weights packed in one word:
+// bytes 2*HALF and 2*HALF + 1 of w (little-endian) go to the low and high
+// 16-bit halves; a half is 0xFFFF iff its byte is >= the threshold t, where
+// tm1 holds t - 1 (t >= 1) in both halves: (t - 1) - byte is negative as a
+// 16-bit integer exactly when byte >= t.
+template <int HALF>
+__device__ __forceinline__ uint32_t keep_mask16(uint32_t w, uint32_t tm1) {
+  const uint32_t x = __builtin_amdgcn_perm(0u, w, HALF ? 0x0c030c02u : 0x0c010c00u);
+  const u16x2 d = __builtin_bit_cast(u16x2, tm1) - __builtin_bit_cast(u16x2, x);
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, d) >> (short)15);
 }
 
 __device__ __forceinline__ f32x16 zero16() {

@@ -45,6 +45,12 @@
 //     weights up to 2^16 without loss of relative precision.
 //   * causal tiles above the diagonal are never visited; only tiles that
 //     straddle the diagonal or the sequence end are masked.
+//   * dropout (a compile-time variant, as "FlashAttention: The Algorithm That
+//     Beat the Memory Wall", "Why Templates Matter Here", describes the
+//     kernel family): each weight is kept or zeroed by one byte of a
+//     counter-based generator drawn in registers during the softmax, so no
+//     mask is stored; the dropped weights still count in l, and O is scaled
+//     by 256 / (256 - t) at the end (t the byte threshold).
 //   * the first-tile NaN of "exp(-inf - -inf)" ("S12 FlashAttention", "Build
 //     it / Implementation") is avoided by substituting 0 for a -inf reference
 //     when forming exponents.
@@ -86,8 +92,9 @@ __device__ __forceinline__ int swz_v(int ch, int r, int c) {
   return ch == 16 ? c ^ (4 * (r & 3)) : c ^ (4 * ((r >> 1) & 1));
 }
 
-template <int D, bool CAUSAL, bool PAGED>
+template <int D, bool CAUSAL, bool PAGED, bool DROP>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
+  static_assert(!(PAGED && DROP), "dropout is built for dense and packed prefill");
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int TILE = kBc * D;            // elements per K or V tile
   constexpr int RPI = 512 / D;              // rows per 1 KB DMA instruction
@@ -190,6 +197,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+  // Dropout: this lane's row id, its index in the LSE layout.
+  const uint64_t rid = (uint64_t)(lse_base + row);
   float m_run = -INFINITY;  // base-2 reference max of this lane's row
   float l_run = 0.f;        // this half-wave's share of the running sum of weights
   const float c = p.scale_log2;
@@ -305,6 +314,11 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // Softmax of tile t in place (scores -> weights), producing the bf16 B
   // operands of the P.V product.
   bf16x8 pf[4];
+  // Dropout bytes of the tile: dw[kc][0] holds the bytes of keys 16kc + 4hi
+  // + 0..3 of this lane's row, dw[kc][1] those of keys 16kc + 8 + 4hi + 0..3
+  // (words hi and 2 + hi of the generator's output for the 16-key group kc).
+  uint32_t dw[4][2];
+  const uint32_t tm1 = DROP ? (uint32_t)(p.drop_t - 1) * 0x00010001u : 0u;
   // The correction of o found by a softmax is applied at the start of the
   // following P.V phase (o is not touched in between); l is corrected at once.
   bool corr = false;   // the reference moved in the last softmax: o must be scaled by alpha
@@ -339,6 +353,13 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       pw.y = pack_bf16x2(pv[2], pv[3]);
       pw.z = pack_bf16x2(pv[4], pv[5]);
       pw.w = pack_bf16x2(pv[6], pv[7]);
+      if (DROP) {
+        // Dropped weights become zero in P.V only; the sum keeps them.
+        pw.x &= keep_mask16<0>(dw[kc][0], tm1);
+        pw.y &= keep_mask16<1>(dw[kc][0], tm1);
+        pw.z &= keep_mask16<0>(dw[kc][1], tm1);
+        pw.w &= keep_mask16<1>(dw[kc][1], tm1);
+      }
       pf[kc] = __builtin_bit_cast(bf16x8, pw);
     }
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
@@ -355,6 +376,24 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > kend) sacc[kb][r] = -INFINITY;
+    }
+    if (DROP) {
+      // Both halves of the wave hold the same row: lane half hi draws the
+      // 16-key groups 2u + hi, and one swap across the halves hands each
+      // lane the words it needs from the other half's draw (lanes 0..31 keep
+      // words 0 and 2, lanes 32..63 words 1 and 3, of every group).
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 r = philox4x32_10(
+            make_uint4((uint32_t)(4 * t + 2 * u + hi), (uint32_t)rid, (uint32_t)(rid >> 32), p.drop_offset),
+            p.drop_seed_lo, p.drop_seed_hi);
+        const auto w01 = __builtin_amdgcn_permlane32_swap(r.x, r.y, false, false);
+        const auto w23 = __builtin_amdgcn_permlane32_swap(r.z, r.w, false, false);
+        dw[2 * u][0] = w01[0];
+        dw[2 * u + 1][0] = w01[1];
+        dw[2 * u][1] = w23[0];
+        dw[2 * u + 1][1] = w23[1];
+      }
     }
     // Fast path: weights against the current reference m_run, without the
     // tile's row max.  Every weight is at most this lane's partial sum, so a
@@ -506,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // Epilogue: O = o / l, LSE = (m + log2 l) * ln 2, with l the fp32 sum of
   // the weights (P.V took them rounded to bf16).
   const float l_tot = sum_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? p.drop_scale : 1.f);
   // The wave's 32 output rows go through LDS (the tile ring is idle: every
   // tile has been consumed behind the last barrier) so that global stores
   // write whole rows, 16 bytes per lane, instead of 8-byte pieces of 64
@@ -539,9 +578,14 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int64_t nwg = (int64_t)p.num_qtiles * p.heads_q * p.batch;
   if (p.paged)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
+  else if (p.drop_t > 0)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
   return hipGetLastError();
 }
 

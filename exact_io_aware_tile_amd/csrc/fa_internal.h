@@ -52,6 +52,13 @@ struct FwdParams {
   const int32_t* seq_lens_k;
   int32_t max_blocks;
   int64_t p_bs, p_hs, p_ts;  // pool strides: block, head, token
+  // Dropout (bf16, dense and packed; drop_t == 0: none).  The weight of row
+  // r (its index in the LSE layout) on key j of its sequence is kept iff
+  // byte j % 16 of Philox-4x32-10(counter {j / 16, r, r >> 32, drop_offset},
+  // key {seed lo, seed hi}) is >= drop_t; O is then scaled by drop_scale.
+  int32_t drop_t;
+  uint32_t drop_seed_lo, drop_seed_hi, drop_offset;
+  float drop_scale;
 };
 
 // Paged decode: query heads per kv head (one wave serves the whole group),

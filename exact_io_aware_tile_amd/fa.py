@@ -9,6 +9,8 @@ Layouts (see include/fa.h):
     fa_fwd:          q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o like q, lse [B, Hq, Nq]
     fa_fwd_fp8:      as fa_fwd with uint8 E4M3 q/k/v and per-tensor descale factors -> o bf16
     fa_fwd_varlen:   q [T, Hq, d], k/v [T, Hkv, d], cu_seqlens int32 [S+1] -> o, lse [Hq, T]
+    fa_fwd_dropout, fa_fwd_varlen_dropout: as fa_fwd / fa_fwd_varlen (bf16) with dropout
+                     of the weights drawn from (dropout_p, seed, offset)
     fa_fwd_paged:    q [Tq, Hq, d] (chunks packed by cu_seqlens_q int32 [S+1]), pools and
                      block_table as for decode, seq_lens_k int32 [S] -> o like q, lse [Hq, Tq]
     fa_decode_paged: q [B, Hq, d], pools [blocks, Hkv, 16, d] (or any strides with d
@@ -57,6 +59,10 @@ class FwdVarlenArgs(ctypes.Structure):
                 ("dtype", ctypes.c_int), ("scale", _F), ("causal", _I32)]
 
 
+class DropoutArgs(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint32)]
+
+
 class DecodePagedArgs(ctypes.Structure):
     _fields_ = [("q", _P), ("k_pool", _P), ("v_pool", _P), ("pool_stride", _I64 * 3),
                 ("block_table", _P), ("seq_lens", _P), ("o", _P), ("lse", _P),
@@ -76,7 +82,7 @@ class FwdPagedArgs(ctypes.Structure):
                 ("max_blocks_per_seq", _I32), ("num_blocks", _I32), ("scale", _F), ("causal", _I32)]
 
 
-SYMBOLS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
+SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -102,6 +108,10 @@ def lib(path: str = LIB_PATH):
     L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), _P]
     L.fa_fwd_varlen.restype = ctypes.c_int
+    L.fa_fwd_dropout.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(DropoutArgs), _P]
+    L.fa_fwd_dropout.restype = ctypes.c_int
+    L.fa_fwd_varlen_dropout.argtypes = [ctypes.POINTER(FwdVarlenArgs), ctypes.POINTER(DropoutArgs), _P]
+    L.fa_fwd_varlen_dropout.restype = ctypes.c_int
     L.fa_fwd_paged.argtypes = [ctypes.POINTER(FwdPagedArgs), _P]
     L.fa_fwd_paged.restype = ctypes.c_int
     L.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
@@ -162,9 +172,32 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _dropout_args(dropout_p, seed, offset):
+    d = DropoutArgs()
+    d.p = float(dropout_p)
+    d.seed = int(seed) & (2**64 - 1)
+    d.offset = int(offset) & (2**32 - 1)
+    return d
+
+
 def fa_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
            return_lse: bool = True, stream=None):
     """Dense attention.  Returns (o, lse) (lse is None when return_lse is False)."""
+    a, out, lse = _fwd_args(q, k, v, causal, scale, out, lse, return_lse)
+    _check(lib().fa_fwd(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_dropout(q, k, v, *, dropout_p: float, seed: int, offset: int = 0, causal: bool = False,
+                   scale: float | None = None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Dense attention with dropout of the weights (bf16).  Returns (o, lse)."""
+    a, out, lse = _fwd_args(q, k, v, causal, scale, out, lse, return_lse)
+    d = _dropout_args(dropout_p, seed, offset)
+    _check(lib().fa_fwd_dropout(ctypes.byref(a), ctypes.byref(d), _stream(stream)))
+    return out, lse
+
+
+def _fwd_args(q, k, v, causal, scale, out, lse, return_lse):
     torch = _torch()
     _dev(q, k, v, out, lse)
     B, Nq, Hq, d = q.shape
@@ -181,8 +214,7 @@ def fa_fwd(q, k, v, *, causal: bool = False, scale: float | None = None, out=Non
     a.dtype = _dtype_code(q)
     a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     a.causal = int(bool(causal))
-    _check(lib().fa_fwd(ctypes.byref(a), _stream(stream)))
-    return out, lse
+    return a, out, lse
 
 
 def fa_fwd_fp8(q, k, v, descale, *, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -217,6 +249,22 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = True,
                   scale: float | None = None, out=None, lse=None, return_lse: bool = True,
                   stream=None):
     """Packed variable-length attention.  ``max_seqlen`` is a host-side bound."""
+    a, out, lse = _varlen_args(q, k, v, cu_seqlens, max_seqlen, causal, scale, out, lse, return_lse)
+    _check(lib().fa_fwd_varlen(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def fa_fwd_varlen_dropout(q, k, v, cu_seqlens, max_seqlen: int, *, dropout_p: float, seed: int,
+                          offset: int = 0, causal: bool = True, scale: float | None = None, out=None,
+                          lse=None, return_lse: bool = True, stream=None):
+    """Packed variable-length attention with dropout of the weights (bf16)."""
+    a, out, lse = _varlen_args(q, k, v, cu_seqlens, max_seqlen, causal, scale, out, lse, return_lse)
+    d = _dropout_args(dropout_p, seed, offset)
+    _check(lib().fa_fwd_varlen_dropout(ctypes.byref(a), ctypes.byref(d), _stream(stream)))
+    return out, lse
+
+
+def _varlen_args(q, k, v, cu_seqlens, max_seqlen, causal, scale, out, lse, return_lse):
     torch = _torch()
     _dev(q, k, v, out, lse, cu_seqlens)
     if cu_seqlens.dtype != torch.int32:
@@ -237,8 +285,7 @@ def fa_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = True,
     a.dtype = _dtype_code(q)
     a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     a.causal = int(bool(causal))
-    _check(lib().fa_fwd_varlen(ctypes.byref(a), _stream(stream)))
-    return out, lse
+    return a, out, lse
 
 
 def _fwd_paged_args(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,

@@ -265,7 +265,8 @@ def workload(n: int) -> dict:
     Beyond these: 6. bf16 chunked prefill over the paged pool, 16 sequences
     with contexts U{1024..8192}, each adding a causal chunk of its last 512
     tokens, 32 q heads / 8 kv heads, d = 128; 7. workload 2 in FP8 E4M3 with
-    per-tensor descale factors.
+    per-tensor descale factors; 8. workload 2 with attention dropout p = 0.1
+    (the usual training rate), seed 8, offset 0.
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -288,6 +289,11 @@ def workload(n: int) -> dict:
         lens = varlen_lengths(5, 64, 1024, 32768)
         c = paged_case(5, lens, 32, 8, 128, block_size=16)
         c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    if n == 8:
+        c = workload(2)
+        c.update(dropout_p=0.1, seed=8, offset=0,
+                 name="bf16 causal MHA prefill B=4 H=32 N=2048 d=128, dropout p=0.1")
         return c
     if n == 7:
         c = fp8_case(7, 4, 2048, 2048, 32, 32, 128)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_OK = 0,
@@ -166,6 +166,43 @@ typedef struct {
 } fa_fwd_varlen_args;
 
 fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
+
+/*
+ * fa_fwd_dropout / fa_fwd_varlen_dropout -- fa_fwd and fa_fwd_varlen with
+ * dropout of the normalised attention weights, the dropout variant
+ * "FlashAttention: The Algorithm That Beat the Memory Wall"
+ * (repo-explainer.com), "How the Repo Connects Python to Bare-Metal CUDA"
+ * and "Why Templates Matter Here", lists among the kernel's parameters and
+ * specialisations.
+ *
+ * With t = the nearest integer to 256 * p (ties to even), each weight
+ * P[r][j] = exp(s_rj - LSE_r) is kept with probability (256 - t) / 256 and
+ * scaled by 256 / (256 - t), or replaced by 0:
+ *     O[r] = sum_j keep(r, j) * 256 / (256 - t) * P[r][j] * v_j.
+ * LSE is that of the weights before dropout (the same as without it).  The
+ * mask is a function of (seed, offset, row, key) only, so it can be
+ * regenerated exactly: row r is the row's index in the LSE layout
+ * ((b * heads_q + h) * seqlen_q + i for fa_fwd_dropout, h * total_tokens +
+ * token for fa_fwd_varlen_dropout), j is the key's position in its sequence,
+ * and keep(r, j) holds iff byte (j mod 16) (little-endian) of
+ * Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) at counter
+ * {j / 16, r mod 2^32, r / 2^32, offset} under key {seed mod 2^32,
+ * seed / 2^32} is >= t.  Callers advance `offset` (or the seed) between
+ * calls that need independent masks.
+ *
+ * p must be in [0, 1) and round to t <= 255 (FA_ERR_BAD_SHAPE otherwise);
+ * t = 0 runs the plain kernel.  Dropout is built for FA_BF16
+ * (FA_ERR_UNSUPPORTED for FA_F32 with t > 0); all other arguments and
+ * limits are those of fa_fwd / fa_fwd_varlen.
+ */
+typedef struct {
+  double p;        /* dropout probability */
+  uint64_t seed;   /* generator key */
+  uint32_t offset; /* counter word 3 */
+} fa_dropout_args;
+
+fa_status fa_fwd_dropout(const fa_fwd_args *args, const fa_dropout_args *dropout, void *stream);
+fa_status fa_fwd_varlen_dropout(const fa_fwd_varlen_args *args, const fa_dropout_args *dropout, void *stream);
 
 /*
  * fa_fwd_paged -- chunked prefill over a paged KV pool: every sequence

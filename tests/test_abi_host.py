@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 4
+    assert L.fa_abi_version() == declared == 5
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -68,6 +68,7 @@ STRUCTS = {
     "fa_fwd_paged_args": fa.FwdPagedArgs,
     "fa_fwd_fp8_args": fa.FwdFp8Args,
     "fa_decode_paged_args": fa.DecodePagedArgs,
+    "fa_dropout_args": fa.DropoutArgs,
 }
 
 
@@ -178,6 +179,42 @@ def test_fp8_empty_is_noop(L):
     for kw in (dict(batch=0), dict(seqlen_q=0)):
         a = fp8_args(q=None, k=None, v=None, o=None, **kw)
         assert L.fa_fwd_fp8(ctypes.byref(a), None) == fa.FA_OK
+
+
+def dropout_args(p=0.1, seed=1, offset=0):
+    d = fa.DropoutArgs()
+    d.p, d.seed, d.offset = p, seed, offset
+    return d
+
+
+@pytest.mark.parametrize("dkw,kw,status", [
+    (dict(p=-0.1), {}, fa.FA_ERR_BAD_SHAPE),
+    (dict(p=1.0), {}, fa.FA_ERR_BAD_SHAPE),
+    (dict(p=float("nan")), {}, fa.FA_ERR_BAD_SHAPE),
+    (dict(p=255.5 / 256), {}, fa.FA_ERR_BAD_SHAPE),       # rounds to t = 256
+    (dict(p=0.3), dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(p=0.3), dict(heads_q=3, heads_kv=2), fa.FA_ERR_BAD_SHAPE),
+    (dict(p=0.3), dict(q=None), fa.FA_ERR_NULL_POINTER),
+])
+def test_dropout_rejects_before_launch(L, dkw, kw, status):
+    a, d = fwd_args(**kw), dropout_args(**dkw)
+    assert L.fa_fwd_dropout(ctypes.byref(a), ctypes.byref(d), None) == status
+    assert L.fa_last_error()
+    v = varlen_args(**kw)
+    assert L.fa_fwd_varlen_dropout(ctypes.byref(v), ctypes.byref(d), None) == status
+    assert L.fa_last_error()
+
+
+def test_dropout_null_and_noop(L):
+    a, v = fwd_args(), varlen_args()
+    assert L.fa_fwd_dropout(ctypes.byref(a), None, None) == fa.FA_ERR_NULL_POINTER
+    assert L.fa_fwd_varlen_dropout(ctypes.byref(v), None, None) == fa.FA_ERR_NULL_POINTER
+    d = dropout_args(p=0.5)
+    e = fwd_args(q=None, k=None, v=None, o=None, batch=0)
+    assert L.fa_fwd_dropout(ctypes.byref(e), ctypes.byref(d), None) == fa.FA_OK
+    # p rounding to t = 0 is plain attention, allowed for fp32 too
+    e = fwd_args(q=None, k=None, v=None, o=None, batch=0, dtype=fa.FA_F32)
+    assert L.fa_fwd_dropout(ctypes.byref(e), ctypes.byref(dropout_args(p=0.5 / 256)), None) == fa.FA_OK
 
 
 def varlen_args(**kw):
