@@ -9,8 +9,8 @@ already resident in HBM).  K steps are timed between barrier +
 synchronisation with HIP events on the launch stream.  The paged GQA decode
 workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
 same way and reported in "decode"; the long-context, varlen, chunked paged
-prefill, FP8 prefill and dropout prefill workloads are reported in "extra"
-(FP8 against the 5.0 PFLOP/s dense fp8 peak).
+prefill, FP8 prefill, dropout prefill and head_dim 256 prefill workloads are
+reported in "extra" (FP8 against the 5.0 PFLOP/s dense fp8 peak).
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "chunked": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "fp8": ["exact_io_aware_tile_amd/csrc/fa_fwd_fp8.hip"],
     "dropout": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
+    "d256": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16_d256.hip"],
 }
 
 
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "dropout",
-                                                 "copy"],
+                                                 "d256", "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -309,6 +310,10 @@ def main():
     if want("dropout", not args.no_extra):
         case = inputs.workload(8)
         out["dropout"] = (case, run_prefill(fa, case, args.steps, args.warmup, torch, np, "dropout"))
+    if want("d256", not args.no_extra):
+        case = inputs.workload(9)
+        out["d256"] = (case, run_prefill(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2), torch, np,
+                                         "d256"))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np))
@@ -347,7 +352,7 @@ def main():
                           "ms_per_step": round(dres["ms"], 4), "algorithmic_bytes": dres["bytes"],
                           "num_splits": dres["num_splits"], "roofline": dres["roofline"]}
     extra = []
-    for key in ("long", "varlen", "chunked", "fp8", "dropout"):
+    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256"):
         if key in out:
             c, r = out[key]
             extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",

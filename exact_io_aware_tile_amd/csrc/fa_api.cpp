@@ -112,8 +112,8 @@ fa_status fwd_dense(const fa_fwd_args* a, const fa_dropout_args* drop, const cha
     return fail(FA_ERR_BAD_SHAPE, "%s: heads_q (%d) is not a multiple of heads_kv (%d)", fn, a->heads_q,
                 a->heads_kv);
   if (a->dtype != FA_F32 && a->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)a->dtype);
-  if (a->head_dim != 64 && a->head_dim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported 64 and 128", fn, a->head_dim);
+  if (a->head_dim != 64 && a->head_dim != 128 && !(a->head_dim == 256 && a->dtype == FA_BF16))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported 64 and 128 (and 256 for bf16)", fn, a->head_dim);
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
     return fail(FA_ERR_BAD_SHAPE, "%s: scale must be positive and finite", fn);
   fa::FwdParams p{};
@@ -136,7 +136,7 @@ fa_status fwd_dense(const fa_fwd_args* a, const fa_dropout_args* drop, const cha
       (a->k_stride[1] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[1] > fa::kFwdMaxKvRowStrideBf16))
     return fail(FA_ERR_UNSUPPORTED, "%s: bf16 k/v row strides above %lld elements", fn,
                 (long long)fa::kFwdMaxKvRowStrideBf16);
-  const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
+  const int64_t rows = a->dtype == FA_BF16 ? fa::fwd_rows_per_tile_bf16(a->head_dim) : fa::kFwdRowsPerTileF32;
   const int64_t qtiles = (a->seqlen_q + rows - 1) / rows;
   if (qtiles * a->heads_q * a->batch > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
 
@@ -174,8 +174,8 @@ fa_status fwd_varlen(const fa_fwd_varlen_args* a, const fa_dropout_args* drop, c
     return fail(FA_ERR_BAD_SHAPE, "%s: heads_q (%d) is not a multiple of heads_kv (%d)", fn, a->heads_q,
                 a->heads_kv);
   if (a->dtype != FA_F32 && a->dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)a->dtype);
-  if (a->head_dim != 64 && a->head_dim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported 64 and 128", fn, a->head_dim);
+  if (a->head_dim != 64 && a->head_dim != 128 && !(a->head_dim == 256 && a->dtype == FA_BF16))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported 64 and 128 (and 256 for bf16)", fn, a->head_dim);
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
     return fail(FA_ERR_BAD_SHAPE, "%s: scale must be positive and finite", fn);
   fa::FwdParams p{};
@@ -197,7 +197,7 @@ fa_status fwd_varlen(const fa_fwd_varlen_args* a, const fa_dropout_args* drop, c
       (a->k_stride[0] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[0] > fa::kFwdMaxKvRowStrideBf16))
     return fail(FA_ERR_UNSUPPORTED, "%s: bf16 k/v token strides above %lld elements", fn,
                 (long long)fa::kFwdMaxKvRowStrideBf16);
-  const int64_t rows = a->dtype == FA_BF16 ? fa::kFwdRowsPerTileBf16 : fa::kFwdRowsPerTileF32;
+  const int64_t rows = a->dtype == FA_BF16 ? fa::fwd_rows_per_tile_bf16(a->head_dim) : fa::kFwdRowsPerTileF32;
   const int64_t qtiles = (a->max_seqlen + rows - 1) / rows;
   if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
 

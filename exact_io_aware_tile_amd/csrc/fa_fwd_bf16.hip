@@ -594,6 +594,7 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream) {
   if (head_dim == 128) return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
   if (head_dim == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+  if (head_dim == 256) return launch_fwd_bf16_d256(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -9,6 +9,7 @@ namespace fa {
 
 // Query rows handled by one prefill workgroup.
 constexpr int kFwdRowsPerTileBf16 = 256;
+constexpr int kFwdRowsPerTileBf16D256 = 128;  // head_dim 256: 16 rows per wave
 constexpr int kFwdRowsPerTileF32 = 128;
 // The bf16 prefill kernel addresses rows inside a 64-key tile with 32-bit
 // byte offsets: key/value row strides (elements) are limited to 2^24.
@@ -87,6 +88,11 @@ struct DecodeParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_bf16_d256(const FwdParams& p, hipStream_t stream);
+// Query rows per prefill workgroup of the bf16 kernels.
+inline int fwd_rows_per_tile_bf16(int head_dim) {
+  return head_dim == 256 ? kFwdRowsPerTileBf16D256 : kFwdRowsPerTileBf16;
+}
 hipError_t launch_fwd_fp8(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);

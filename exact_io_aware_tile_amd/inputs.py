@@ -266,7 +266,9 @@ def workload(n: int) -> dict:
     with contexts U{1024..8192}, each adding a causal chunk of its last 512
     tokens, 32 q heads / 8 kv heads, d = 128; 7. workload 2 in FP8 E4M3 with
     per-tensor descale factors; 8. workload 2 with attention dropout p = 0.1
-    (the usual training rate), seed 8, offset 0.
+    (the usual training rate), seed 8, offset 0; 9. bf16 causal GQA prefill
+    at head_dim 256, batch 2, 16 q heads / 8 kv heads, N = 4096 (the shape of
+    a head_dim-256 model's prefill).
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -289,6 +291,10 @@ def workload(n: int) -> dict:
         lens = varlen_lengths(5, 64, 1024, 32768)
         c = paged_case(5, lens, 32, 8, 128, block_size=16)
         c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    if n == 9:
+        c = dense_case(9, 2, 4096, 4096, 16, 8, 256, dtype="bf16")
+        c.update(causal=True, name="bf16 causal GQA prefill B=2 Hq=16 Hkv=8 N=4096 d=256")
         return c
     if n == 8:
         c = workload(2)

@@ -78,7 +78,8 @@ typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
  *   lse [batch, heads_q, seqlen_q] fp32, contiguous (written; may be NULL)
  *
  * dtype FA_F32 (fp32 in, fp32 out, fp32 MFMA) or FA_BF16 (bf16 in, bf16 out
- * rounded to nearest-even, fp32 accumulation); head_dim 64 or 128.
+ * rounded to nearest-even, fp32 accumulation); head_dim 64 or 128, and 256
+ * for FA_BF16 (FA_ERR_UNSUPPORTED otherwise).
  * seqlen_q == 0 or batch == 0 is a no-op; seqlen_k == 0 writes O = 0 and
  * LSE = -inf (k and v may then be NULL).  Strides are in elements,
  * non-negative multiples of 16 bytes; for FA_BF16 the k and v sequence
@@ -150,7 +151,7 @@ fa_status fa_fwd_fp8(const fa_fwd_fp8_args *args, void *stream);
  *
  * A query sees only keys of its own sequence (causal in local positions
  * when causal != 0); an empty sequence writes nothing.  dtype FA_BF16 or
- * FA_F32; head_dim 64 or 128.  For FA_BF16 the k and v token strides are at
+ * FA_F32; head_dim 64 or 128, and 256 for FA_BF16.  For FA_BF16 the k and v token strides are at
  * most 2^24 elements (FA_ERR_UNSUPPORTED otherwise).
  */
 typedef struct {

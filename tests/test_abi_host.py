@@ -115,6 +115,7 @@ def fwd_args(**kw):
     (dict(batch=-1), fa.FA_ERR_BAD_SHAPE),
     (dict(seqlen_k=-2), fa.FA_ERR_BAD_SHAPE),
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=256, dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=float("nan")), fa.FA_ERR_BAD_SHAPE),
@@ -276,6 +277,7 @@ def paged_args(**kw):
     (dict(heads_q=7), fa.FA_ERR_BAD_SHAPE),
     (dict(total_q=-1), fa.FA_ERR_BAD_SHAPE),
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=256), fa.FA_ERR_UNSUPPORTED),
     (dict(block_size=32), fa.FA_ERR_UNSUPPORTED),
     (dict(max_seqlen_k=20 * 16 + 1), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE),

@@ -71,7 +71,8 @@ def kept_counts(o, n, s):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", [(2, 300, 3, 64), (1, 1000, 2, 128), (1, 64, 1, 64), (1, 1, 2, 128)])
+@pytest.mark.parametrize("shape", [(2, 300, 3, 64), (1, 1000, 2, 128), (1, 64, 1, 64), (1, 1, 2, 128),
+                                   (2, 300, 3, 256), (1, 33, 1, 256)])
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
 def test_keep_decisions_bitwise(gpu, shape, causal, p):
     B, N, H, d = shape
@@ -125,6 +126,8 @@ DENSE = [
     (1, 1000, 1000, 2, 2, 128),
     (1, 17, 200, 2, 2, 128),
     (1, 200, 70, 2, 2, 64),
+    (1, 300, 300, 4, 2, 256),
+    (1, 70, 200, 2, 2, 256),
 ]
 
 
@@ -146,7 +149,7 @@ def test_dense_dropout_parity(gpu, shape, causal, p):
     assert torch.equal(lse, lse_plain), "LSE must not depend on dropout"
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_varlen_dropout_parity(gpu, d):
     lens = [1, 130, 0, 64, 257, 7, 128]
     case = inputs.varlen_case(400 + d, lens, 4, 2, d, dtype="bf16")

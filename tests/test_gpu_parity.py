@@ -97,6 +97,54 @@ def test_dense_parity(gpu, shape, causal, dtype):
     check(og, lg, o_ref, lse_ref, dtype, f"{shape} causal={causal} {dtype}")
 
 
+D256_SHAPES = [
+    # B, Nq, Nk, Hq, Hkv, d -- head_dim 256 (16 rows per wave, 32-key tiles)
+    (1, 1, 1, 1, 1, 256),
+    (2, 17, 17, 2, 2, 256),
+    (1, 31, 31, 2, 1, 256),
+    (1, 127, 127, 2, 1, 256),
+    (1, 128, 128, 1, 1, 256),
+    (2, 129, 129, 4, 2, 256),
+    (1, 300, 300, 3, 1, 256),
+    (1, 1000, 1000, 2, 2, 256),
+    (1, 17, 200, 2, 2, 256),
+    (1, 200, 70, 2, 2, 256),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", D256_SHAPES)
+def test_d256_parity(gpu, shape, causal):
+    B, Nq, Nk, Hq, Hkv, d = shape
+    case = inputs.dense_case(500 + Nq, B, Nq, Nk, Hq, Hkv, d, dtype="bf16")
+    og, lg, o_ref, lse_ref = run_dense(gpu, case, causal)
+    check(og, lg, o_ref, lse_ref, "bf16", f"{shape} causal={causal} d=256")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_d256_varlen_parity(gpu, causal):
+    lens = [1, 130, 0, 64, 257, 7, 128, 31]
+    case = inputs.varlen_case(256, lens, 4, 2, 256, dtype="bf16")
+    og, lg, o_ref, lse_ref = run_varlen(gpu, case, causal)
+    check(og, lg, o_ref, lse_ref, "bf16", f"varlen d=256 causal={causal}")
+
+
+def test_d256_workload_sampled(gpu):
+    case = inputs.workload(9)
+    B, N, H = case["batch"], case["nq"], case["hq"]
+    rows = sample_rows(np.random.default_rng(9), B, H, N, 256)
+    og, lg, o_ref, lse_ref = run_dense(gpu, case, case["causal"], rows=rows)
+    check(og, lg, o_ref, lse_ref, "bf16", "d=256 workload sampled rows")
+
+
+def test_d256_empty_keys(gpu):
+    q = torch.randn(1, 40, 2, 256, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(1, 0, 2, 256, device="cuda", dtype=torch.bfloat16)
+    o, lse = gpu.fa_fwd(q, k, k, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
 def test_workload1_fp32(gpu):
     case = inputs.workload(1)
     og, lg, o_ref, lse_ref = run_dense(gpu, case, case["causal"])
