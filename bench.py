@@ -105,6 +105,44 @@ def time_steps(fn, steps, warmup, torch):
     return t0.elapsed_time(t1) / steps, wall / steps * 1e3  # ms per step (events, wall)
 
 
+def time_cold(fn, reps, torch, flush):
+    """Per-launch HIP-event times (ms) with a write of FLUSH (larger than the
+    256 MB last-level cache) between launches, outside the timed window."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for r in range(reps):
+        flush.fill_(r & 0x7F)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    times.sort()
+    return times[0], times[len(times) // 2]
+
+
+def copy_bandwidth(torch, reps=10):
+    """Device-to-device copy of 1 GiB: bytes read + written per second (GB/s),
+    a measured ceiling for a streaming kernel on this GPU."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def prefill_flops(case) -> float:
     d, B, H = case["d"], case["batch"], case["hq"]
     nq, nk = case["nq"], case["nk"]
@@ -139,7 +177,7 @@ def cpu_baseline(case, seconds, np):
                       f"(b, h, i) rows, fp64 materialised-score oracle, {el:.1f} s wall"}
 
 
-def run_prefill(fa, case, steps, warmup, torch, np, kind):
+def run_prefill(fa, case, steps, warmup, torch, np, kind, flush=None):
     q, k, v = (bf16_dev(case[n], torch, np) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty((case["batch"], case["hq"], case["nq"]), dtype=torch.float32, device="cuda")
@@ -156,8 +194,13 @@ def run_prefill(fa, case, steps, warmup, torch, np, kind):
     flops = prefill_flops(case)
     tf = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(kind)
+    cold = None
+    if flush is not None:
+        mn, med = time_cold(step, 20, torch, flush)
+        cold = {"min_us": round(mn * 1e3, 1), "median_us": round(med * 1e3, 1),
+                "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2)}
     return {
-        "ms": ms, "wall_ms": wall_ms, "tflops": tf, "flops": flops,
+        "ms": ms, "wall_ms": wall_ms, "tflops": tf, "flops": flops, "cold": cold,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
@@ -226,7 +269,7 @@ def run_fp8(fa, case, steps, warmup, torch, np):
                          "traffic": measured_traffic("fp8")}}
 
 
-def run_decode(fa, case, steps, warmup, torch, np):
+def run_decode(fa, case, steps, warmup, torch, np, flush=None):
     q = bf16_dev(case["q"], torch, np)
     kp = bf16_dev(case["k_pool"], torch, np)
     vp = bf16_dev(case["v_pool"], torch, np)
@@ -250,7 +293,12 @@ def run_decode(fa, case, steps, warmup, torch, np):
     nbytes = kv_bytes + other
     gbs = nbytes / (ms * 1e-3) / 1e9
     traffic = measured_traffic("decode")
-    return {"ms": ms, "gbs": gbs, "bytes": nbytes, "kv_bytes": kv_bytes, "num_splits": splits,
+    cold = None
+    if flush is not None:
+        mn, med = time_cold(step, 20, torch, flush)
+        cold = {"min_us": round(mn * 1e3, 1), "median_us": round(med * 1e3, 1),
+                "gbs_at_median": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    return {"ms": ms, "gbs": gbs, "bytes": nbytes, "kv_bytes": kv_bytes, "num_splits": splits, "cold": cold,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}}
 
@@ -289,9 +337,12 @@ def main():
         return name in only if only else default
 
     out = {}
+    # 512 MB written between cold launches (outside their timed window) so
+    # that no input stays in the 256 MB last-level cache.
+    flush = None if only else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     if want("prefill"):
         case = inputs.workload(2)
-        res = run_prefill(fa, case, args.steps, args.warmup, torch, np, "prefill")
+        res = run_prefill(fa, case, args.steps, args.warmup, torch, np, "prefill", flush)
         out["prefill"] = (case, res)
     if want("long", not args.no_extra):
         case = inputs.workload(3)
@@ -316,7 +367,7 @@ def main():
                                          "d256"))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
-        out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np))
+        out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, flush))
     if want("copy", False):
         run_copy(torch, args.steps)
 
@@ -345,12 +396,16 @@ def main():
                    "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 3)},
         "roofline": res["roofline"],
         "kernel_ms": round(res["ms"], 4),
+        "cold": res["cold"],
     }
     if "decode" in out:
         dcase, dres = out["decode"]
         line["decode"] = {"workload": dcase["name"], "value": round(dres["gbs"], 1), "unit": "GB/s",
                           "ms_per_step": round(dres["ms"], 4), "algorithmic_bytes": dres["bytes"],
-                          "num_splits": dres["num_splits"], "roofline": dres["roofline"]}
+                          "num_splits": dres["num_splits"], "roofline": dres["roofline"], "cold": dres["cold"]}
+        del flush
+        flush = None
+        line["decode"]["copy_gbs"] = round(copy_bandwidth(torch), 1)
     extra = []
     for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256"):
         if key in out:
