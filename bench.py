@@ -10,7 +10,8 @@ synchronisation with HIP events on the launch stream.  The paged GQA decode
 workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
 same way and reported in "decode"; the long-context, varlen, chunked paged
 prefill, FP8 prefill, dropout prefill and head_dim 256 prefill workloads are
-reported in "extra" (FP8 against the 5.0 PFLOP/s dense fp8 peak).
+reported in "extra" (FP8 against the 5.0 PFLOP/s dense fp8 peak), as is a
+head_dim 256 paged decode workload (GB/s).
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -40,6 +41,7 @@ KERNEL_SOURCES = {
     "fp8": ["exact_io_aware_tile_amd/csrc/fa_fwd_fp8.hip"],
     "dropout": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "d256": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16_d256.hip"],
+    "decode_d256": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
 }
 
 
@@ -54,7 +56,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "dropout",
-                                                 "d256", "copy"],
+                                                 "d256", "decode_d256", "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -269,7 +271,7 @@ def run_fp8(fa, case, steps, warmup, torch, np):
                          "traffic": measured_traffic("fp8")}}
 
 
-def run_decode(fa, case, steps, warmup, torch, np, flush=None):
+def run_decode(fa, case, steps, warmup, torch, np, flush=None, kind="decode"):
     q = bf16_dev(case["q"], torch, np)
     kp = bf16_dev(case["k_pool"], torch, np)
     vp = bf16_dev(case["v_pool"], torch, np)
@@ -292,7 +294,7 @@ def run_decode(fa, case, steps, warmup, torch, np, flush=None):
     other = float(q.numel() * 2 + o.numel() * 2 + 4 * ((L + bs - 1) // bs).sum() + 4 * L.size)
     nbytes = kv_bytes + other
     gbs = nbytes / (ms * 1e-3) / 1e9
-    traffic = measured_traffic("decode")
+    traffic = measured_traffic(kind)
     cold = None
     if flush is not None:
         mn, med = time_cold(step, 20, torch, flush)
@@ -365,6 +367,9 @@ def main():
         case = inputs.workload(9)
         out["d256"] = (case, run_prefill(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2), torch, np,
                                          "d256"))
+    if want("decode_d256", not args.no_extra):
+        case = inputs.workload(10)
+        out["decode_d256"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, kind="decode_d256"))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, flush))
@@ -407,11 +412,15 @@ def main():
         flush = None
         line["decode"]["copy_gbs"] = round(copy_bandwidth(torch), 1)
     extra = []
-    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256"):
+    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256", "decode_d256"):
         if key in out:
             c, r = out[key]
-            extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",
-                          "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]})
+            if "gbs" in r:
+                extra.append({"workload": c["name"], "value": round(r["gbs"], 1), "unit": "GB/s",
+                              "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]})
+            else:
+                extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",
+                              "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]})
     if extra:
         line["extra"] = extra
     line["context"] = ("pages' figures (other hardware): 2-4x wall-clock over standard attention; "

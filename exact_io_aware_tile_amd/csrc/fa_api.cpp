@@ -49,7 +49,6 @@ bool strides_ok(const int64_t* s, int n, int64_t elems16) {
 float scale_log2(float scale) { return (float)((double)scale * 1.4426950408889634073599); }
 
 constexpr int kDecodeBlock = 16;
-constexpr int kDecodeDim = 128;
 
 fa_status check_decode(const fa_decode_paged_args* a) {
   if (!a) return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: args is NULL");
@@ -63,8 +62,8 @@ fa_status check_decode(const fa_decode_paged_args* a) {
   if (group > fa::kDecodeMaxGroup)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: heads_q / heads_kv = %d, supported up to %d", group,
                 fa::kDecodeMaxGroup);
-  if (a->head_dim != kDecodeDim)
-    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d, supported 128", a->head_dim);
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: head_dim %d, supported 64, 128 and 256", a->head_dim);
   if (a->block_size != kDecodeBlock)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode_paged: block_size %d, supported 16", a->block_size);
   if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size)
@@ -83,7 +82,8 @@ fa_status check_decode(const fa_decode_paged_args* a) {
 
 // Parts the key-block list is cut into; -1 if the device cannot be queried.
 int decode_parts(const fa_decode_paged_args* a) {
-  return fa::decode_num_parts(a->num_splits, a->batch, a->heads_q, a->heads_q / a->heads_kv, a->max_seq_len);
+  return fa::decode_num_parts(a->num_splits, a->batch, a->heads_q, a->heads_q / a->heads_kv, a->max_seq_len,
+                              a->head_dim);
 }
 
 
@@ -369,7 +369,7 @@ FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) {
     fail(FA_ERR_HIP, "fa_decode_paged_workspace_size: cannot query the current device");
     return 0;
   }
-  return fa::decode_workspace_bytes(parts, a->batch, a->heads_q);
+  return fa::decode_workspace_bytes(parts, a->batch, a->heads_q, a->head_dim);
 }
 
 FA_EXPORT int32_t fa_decode_paged_num_splits(const fa_decode_paged_args* a) {
@@ -399,7 +399,7 @@ FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream)
     return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: q, pools, o and workspace must be 16-byte aligned");
   const int parts = decode_parts(a);
   if (parts < 1) return fail(FA_ERR_HIP, "fa_decode_paged: cannot query the current device");
-  const size_t need = fa::decode_workspace_bytes(parts, a->batch, a->heads_q);
+  const size_t need = fa::decode_workspace_bytes(parts, a->batch, a->heads_q, a->head_dim);
   if (a->workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode_paged: workspace %zu bytes, need %zu", a->workspace_bytes,
                 need);
@@ -418,7 +418,7 @@ FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream)
   p.num_splits = parts;
   const size_t rows = (size_t)a->heads_q * (size_t)(parts + a->batch);
   p.ws_o = (float*)a->workspace;
-  p.ws_ml = p.ws_o + rows * kDecodeDim;
+  p.ws_ml = p.ws_o + rows * a->head_dim;
   p.batch = a->batch;
   p.heads_q = a->heads_q;
   p.heads_kv = a->heads_kv;
@@ -426,7 +426,7 @@ FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream)
   p.max_blocks = a->max_blocks_per_seq;
   p.max_seq_len = a->max_seq_len;
   p.scale_log2 = scale_log2(a->scale);
-  const hipError_t e = fa::launch_decode_paged(p, (hipStream_t)stream);
+  const hipError_t e = fa::launch_decode_paged(p, a->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode_paged: launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -54,7 +54,6 @@ namespace fa {
 namespace {
 
 constexpr int kBlock = 16;
-constexpr int kD = 128;
 constexpr float kLazyLog2 = 8.f;    // largest weight 2^8 against a stale reference
 constexpr float kInitMax = -1e30f;  // finite initial reference max
 constexpr int kMlStride = 4;        // workspace floats per partial: m, l, lb, unused
@@ -153,18 +152,42 @@ __device__ __forceinline__ uint4 load_stream(const char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Physical 16-byte chunk of logical chunk c in value row r of the LDS copy.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 3) + 8 * ((r >> 2) & 1)); }
+// Physical 16-byte chunk of logical chunk c in value row r of the LDS copy
+// (D / 8 chunks per row).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return D >= 128 ? c ^ (2 * (r & 3) + 8 * ((r >> 2) & 1)) : c ^ (2 * (r & 3));
+}
 
 // One block as this lane loads it: k[s] = token l%16, dims 32s + 8(l/16)
-// .. +7 (score A operand); v[s] = token 4s + l/16, dims 8(l%16) .. +7.
+// .. +7 (score A operand); v[s] = token s * 64/(D/8) + l / (D/8), dims
+// 8(l % (D/8)) .. +7 (D/32 loads each).
+template <int D>
 struct Blk {
-  uint4 k[4];
-  uint4 v[4];
+  uint4 k[D / 32];
+  uint4 v[D / 32];
 };
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_kernel(
-    const DecodeParams p) {
+// Blocks in flight per wave (the register ring): four at head_dim 64 and
+// 128, two at 256, where a block is 16 KB per operand and the ring would
+// otherwise take every register.
+template <int D>
+constexpr int ring_depth() { return D == 256 ? 2 : 4; }
+
+// Waves per SIMD the split kernel is built for: two, or one at head_dim 256
+// (its ring, accumulator and Q fragments need more than 256 registers; the
+// rest goes to the accumulation registers).
+template <int D>
+constexpr int split_waves_per_simd() { return D == 256 ? 1 : 2; }
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<D>(),
+                                                                     split_waves_per_simd<D>()))) void
+decode_split_kernel(const DecodeParams p) {
+  constexpr int kD = D;
+  constexpr int NS = D / 32;       // 32-dim steps of the score product; value loads per lane
+  constexpr int VCH = D / 8;       // 16-byte chunks of a value row
+  constexpr int VTPL = 64 / VCH;   // value rows per load instruction
   const int part = blockIdx.x;
   const int g = blockIdx.y;  // kv head; query heads g*G .. g*G + G - 1
   const int G = p.group;
@@ -193,44 +216,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // block (the host keeps it below 2^31).
   const char* __restrict__ kpool = (const char*)p.k_pool + (int64_t)g * p.p_hs * 2;
   const char* __restrict__ vpool = (const char*)p.v_pool + (int64_t)g * p.p_hs * 2;
-  uint32_t koff[4], voff[4];
+  uint32_t koff[NS], voff[NS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < NS; ++s) {
     koff[s] = (uint32_t)((n * p.p_ts + 32 * s + 8 * j) * 2);
-    voff[s] = (uint32_t)(((4 * s + j) * p.p_ts + 8 * n) * 2);
+    voff[s] = (uint32_t)(((s * VTPL + lane / VCH) * p.p_ts + 8 * (lane % VCH)) * 2);
   }
 
   // Q of head n as the B operand of the score product (zero for columns
   // past the group).
-  uint4 qf[4];
+  uint4 qf[NS];
   auto load_q = [&](int b) {
     const uint16_t* qr = (const uint16_t*)p.q + (int64_t)b * p.q_bs + (int64_t)(g * G + n) * p.q_hs + 8 * j;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = n < G ? *(const uint4*)(qr + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
+    for (int s = 0; s < NS; ++s) qf[s] = n < G ? *(const uint4*)(qr + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
   };
   load_q(pc.b);
 
-  f32x4 o[8];      // O^T: o[db][r] = dim 16db + 4j + r of head n
+  f32x4 o[D / 16];  // O^T: o[db][r] = dim 16db + 4j + r of head n
   float m, l, lb;  // reference max (base 2), fp32 weight sum, bf16 weight sum
   auto reset = [&]() {
     m = kInitMax;
     l = 0.f;
     lb = 0.f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = zero4();
+    for (int db = 0; db < D / 16; ++db) o[db] = zero4();
   };
   reset();
 
   int n_issued = 0;
-  auto issue = [&](Blk& B) {
+  auto issue = [&](Blk<D>& B) {
     if (n_issued < n_units) {
       const int64_t base = (int64_t)p.block_table[(int64_t)ic.b * p.max_blocks + ic.blk] * p.p_bs * 2;
       const char* kb = kpool + base;
       const char* vb = vpool + base;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) B.k[s] = load_stream(kb + koff[s]);
+      for (int s = 0; s < NS; ++s) B.k[s] = load_stream(kb + koff[s]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) B.v[s] = load_stream(vb + voff[s]);
+      for (int s = 0; s < NS; ++s) B.v[s] = load_stream(vb + voff[s]);
       if (++n_issued < n_units) cursor_next(p, ic);
     }
   };
@@ -241,17 +264,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   // One block through the recurrence; tokens at or past VALID hold no key
   // (only a sequence's last block has such tokens).
-  auto process = [&](const Blk& B, int valid) {
+  auto process = [&](const Blk<D>& B, int valid) {
     // Values to LDS (row = token, swizzled chunks).
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = 4 * s + j;
-      *(uint4*)&v_s[r * kD + swz(r, n) * 8] = B.v[s];
+    for (int s = 0; s < NS; ++s) {
+      const int r = s * VTPL + lane / VCH;
+      *(uint4*)&v_s[r * kD + swz<D>(r, lane % VCH) * 8] = B.v[s];
     }
     // Scores: sc[r] = S[token 4j + r][head n].
     f32x4 sc = zero4();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < NS; ++s)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, B.k[s]),
                                                   __builtin_bit_cast(bf16x8, qf[s]), sc, 0, 0, 0);
     float x[4];
@@ -267,7 +290,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       l *= al;
       lb *= al;
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[db][r] *= al;
     }
@@ -292,9 +315,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // dim 16db + n of tokens 4j .. 4j+3.
     const int vr = 4 * j + tk;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < D / 16; ++db) {
       const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&v_s[vr * kD + swz(vr, 2 * db + (tq >> 1)) * 8 + 4 * (tq & 1)]);
+          (lds_i16x4*)&v_s[vr * kD + swz<D>(vr, 2 * db + (tq >> 1)) * 8 + 4 * (tq & 1)]);
       uint2 w = __builtin_bit_cast(uint2, vt);
       w.x &= keep0;
       w.y &= keep1;
@@ -314,13 +337,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       const int64_t row = (int64_t)(g * G + n) * S + part + b;
       float* dst = p.ws_o + row * kD + 4 * j;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *(f32x4*)(dst + 16 * db) = o[db];
+      for (int db = 0; db < D / 16; ++db) *(f32x4*)(dst + 16 * db) = o[db];
       if (j == 0) *(float4*)(p.ws_ml + row * kMlStride) = make_float4(m, lt, lbt, 0.f);
     }
   };
 
   int n_done = 0;
-  auto step = [&](const Blk& B) {
+  auto step = [&](const Blk<D>& B) {
     if (n_done >= n_units) return;
     const bool last_blk = pc.blk == pc.nb - 1;
     process(B, last_blk ? pc.L - pc.blk * kBlock : kBlock);
@@ -340,29 +363,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // The scheduling barriers keep each ring refill where it is written, three
   // blocks ahead of its use, instead of letting the scheduler sink the loads
   // next to their consumers.
-  Blk A, B, C, D;
-  issue(A);
-  issue(B);
-  issue(C);
-  issue(D);
+  Blk<D> R0, R1, R2, R3;
+  issue(R0);
+  issue(R1);
+  if constexpr (ring_depth<D>() == 4) {
+    issue(R2);
+    issue(R3);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  for (int u = 0; u < n_units; u += 4) {
-    step(A);
+  for (int u = 0; u < n_units; u += ring_depth<D>()) {
+    step(R0);
     __builtin_amdgcn_sched_barrier(0);
-    issue(A);
+    issue(R0);
     __builtin_amdgcn_sched_barrier(0);
-    step(B);
+    step(R1);
     __builtin_amdgcn_sched_barrier(0);
-    issue(B);
+    issue(R1);
     __builtin_amdgcn_sched_barrier(0);
-    step(C);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(C);
-    __builtin_amdgcn_sched_barrier(0);
-    step(D);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(D);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ring_depth<D>() == 4) {
+      step(R2);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(R2);
+      __builtin_amdgcn_sched_barrier(0);
+      step(R3);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(R3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -371,7 +398,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // its first and last blocks and every non-empty part between; part w holds
 // list positions [w*U/P, (w+1)*U/P), so position x lies in part
 // ceil((x+1)*P/U) - 1.
+template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p) {
+  constexpr int kD = D;
+  constexpr int DPL = D / 64;  // output dims per lane
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
@@ -385,7 +415,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
 
   const int P = p.num_splits;
   const int S = P + p.batch;
-  float M = -INFINITY, l = 0.f, lb = 0.f, o0 = 0.f, o1 = 0.f;
+  float M = -INFINITY, l = 0.f, lb = 0.f;
+  float oa[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) oa[i] = 0.f;
   if (nb > 0) {
     const int w0 = (int)(((int64_t)(first + 1) * P + U - 1) / U) - 1;
     const int w1 = (int)(((int64_t)(first + nb) * P + U - 1) / U) - 1;
@@ -400,50 +433,67 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
       const float wt = exp2_fast(ml.x - M);
       l = __builtin_fmaf(wt, ml.y, l);
       lb = __builtin_fmaf(wt, ml.z, lb);
-      const float2 v = *(const float2*)(p.ws_o + (row0 + w) * kD + 2 * lane);
-      o0 = __builtin_fmaf(wt, v.x, o0);
-      o1 = __builtin_fmaf(wt, v.y, o1);
+      const float* v = p.ws_o + (row0 + w) * kD + DPL * lane;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) oa[i] = __builtin_fmaf(wt, v[i], oa[i]);
     }
   }
   // o / lb: the weights P.V used, so the row is a convex combination of
   // value rows up to fp32 rounding; LSE from the fp32 weights.
   const float inv = lb > 0.f ? 1.f / lb : 0.f;
   uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.o_bs + (int64_t)h * p.o_hs;
-  *(uint32_t*)(orow + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+  if constexpr (DPL == 1) {
+    orow[lane] = (uint16_t)(pack_bf16x2(oa[0] * inv, 0.f) & 0xFFFFu);
+  } else {
+#pragma unroll
+    for (int i = 0; i < DPL; i += 2) *(uint32_t*)(orow + DPL * lane + i) = pack_bf16x2(oa[i] * inv, oa[i + 1] * inv);
+  }
   if (p.lse && lane == 0)
     p.lse[(int64_t)b * p.heads_q + h] = l > 0.f ? (M + log2_fast(l)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
-int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len) {
+int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim) {
   if (num_splits > 0) return num_splits;
   // One part per wave slot of the device (the split kernel is built for two
-  // waves per SIMD, eight per CU), spread over the kv heads; no more parts
-  // than about one per 4 blocks of the largest possible batch.
+  // waves per SIMD, eight per CU; one and four at head_dim 256), spread over
+  // the kv heads; no more parts than about one per 4 blocks of the largest
+  // possible batch.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   const int64_t heads_kv = group > 0 ? heads_q / group : 1;
-  int64_t parts = (int64_t)cus * kSplitWavesPerCu / (heads_kv > 0 ? heads_kv : 1);
+  const int waves_per_cu = head_dim == 256 ? 4 * split_waves_per_simd<256>() : kSplitWavesPerCu;
+  int64_t parts = (int64_t)cus * waves_per_cu / (heads_kv > 0 ? heads_kv : 1);
   const int64_t max_units = (int64_t)batch * ((max_seq_len + kBlock - 1) / kBlock);
   if (parts > (max_units + 3) / 4) parts = (max_units + 3) / 4;
   if (parts < 1) parts = 1;
   return (int)parts;
 }
 
-size_t decode_workspace_bytes(int parts, int batch, int heads_q) {
+size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim) {
   const size_t rows = (size_t)heads_q * (size_t)(parts + batch);
-  return rows * (kD + kMlStride) * sizeof(float);
+  return rows * ((size_t)head_dim + kMlStride) * sizeof(float);
 }
 
-hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel, dim3(p.num_splits, p.heads_kv), dim3(64), 0, stream, p);
+namespace {
+template <int D>
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.num_splits, p.heads_kv), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.heads_q, p.batch), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.heads_q, p.batch), dim3(64), 0, stream, p);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_paged(const DecodeParams& p, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return launch_decode<128>(p, stream);
+  if (head_dim == 64) return launch_decode<64>(p, stream);
+  if (head_dim == 256) return launch_decode<256>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

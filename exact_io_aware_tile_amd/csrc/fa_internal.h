@@ -95,10 +95,10 @@ inline int fwd_rows_per_tile_bf16(int head_dim) {
 }
 hipError_t launch_fwd_fp8(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_decode_paged(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_paged(const DecodeParams& p, int head_dim, hipStream_t stream);
 // Parts for a requested num_splits (0: one per wave slot of the current
 // device, or of a 256-CU device when none can be queried).
-int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len);
-size_t decode_workspace_bytes(int parts, int batch, int heads_q);
+int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim);
+size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim);
 
 }  // namespace fa

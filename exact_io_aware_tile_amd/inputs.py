@@ -268,7 +268,8 @@ def workload(n: int) -> dict:
     per-tensor descale factors; 8. workload 2 with attention dropout p = 0.1
     (the usual training rate), seed 8, offset 0; 9. bf16 causal GQA prefill
     at head_dim 256, batch 2, 16 q heads / 8 kv heads, N = 4096 (the shape of
-    a head_dim-256 model's prefill).
+    a head_dim-256 model's prefill); 10. bf16 paged GQA decode at head_dim
+    256, batch 32, 16 q heads / 8 kv heads, lengths U{1024..16384}.
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -291,6 +292,11 @@ def workload(n: int) -> dict:
         lens = varlen_lengths(5, 64, 1024, 32768)
         c = paged_case(5, lens, 32, 8, 128, block_size=16)
         c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    if n == 10:
+        lens = varlen_lengths(10, 32, 1024, 16384)
+        c = paged_case(10, lens, 16, 8, 256, block_size=16)
+        c.update(name="bf16 paged GQA decode B=32 Hq=16 Hkv=8 d=256 L~U{1024..16384} block 16")
         return c
     if n == 9:
         c = dense_case(9, 2, 4096, 4096, 16, 8, 256, dtype="bf16")

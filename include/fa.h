@@ -151,8 +151,8 @@ fa_status fa_fwd_fp8(const fa_fwd_fp8_args *args, void *stream);
  *
  * A query sees only keys of its own sequence (causal in local positions
  * when causal != 0); an empty sequence writes nothing.  dtype FA_BF16 or
- * FA_F32; head_dim 64 or 128, and 256 for FA_BF16.  For FA_BF16 the k and v token strides are at
- * most 2^24 elements (FA_ERR_UNSUPPORTED otherwise).
+ * FA_F32; head_dim 64 or 128, and 256 for FA_BF16.  For FA_BF16 the k and
+ * v token strides are at most 2^24 elements (FA_ERR_UNSUPPORTED otherwise).
  */
 typedef struct {
   const void *q, *k, *v;
@@ -291,7 +291,8 @@ fa_status fa_fwd_paged(const fa_fwd_paged_args *args, void *stream);
  *       ignored.  Holds heads_q * (parts + batch) partial states of
  *       head_dim + 4 floats.
  *
- * Supported: bf16, head_dim 128, block_size 16, heads_q / heads_kv <= 16.
+ * Supported: bf16, head_dim 64, 128 or 256, block_size 16,
+ * heads_q / heads_kv <= 16.
  */
 typedef struct {
   const void *q;

@@ -326,7 +326,7 @@ def decode_args(**kw):
     (dict(heads_q=30), fa.FA_ERR_BAD_SHAPE),
     (dict(heads_kv=1), fa.FA_ERR_UNSUPPORTED),   # group 32 > 16
     (dict(pool_stride=[8 * 16 * 128, 16 * 128, (1 << 26) + 8]), fa.FA_ERR_UNSUPPORTED),
-    (dict(head_dim=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
     (dict(block_size=32), fa.FA_ERR_UNSUPPORTED),
     (dict(max_seq_len=64 * 16 + 1), fa.FA_ERR_BAD_SHAPE),
     (dict(batch=-3), fa.FA_ERR_BAD_SHAPE),
@@ -341,6 +341,12 @@ def test_decode_rejects_before_launch(L, kw, status):
     a = decode_args(**kw)
     assert L.fa_decode_paged(ctypes.byref(a), None) == status
     assert L.fa_last_error()
+
+
+def test_decode_workspace_scales_with_head_dim(L):
+    for d in (64, 128, 256):
+        a = decode_args(num_splits=5, head_dim=d)
+        assert L.fa_decode_paged_workspace_size(ctypes.byref(a)) == 32 * (5 + 4) * (d + 4) * 4
 
 
 def test_decode_sizes(L):
@@ -362,7 +368,7 @@ def test_decode_sizes(L):
     a = decode_args(max_seq_len=64 * 16, max_blocks_per_seq=64, batch=64)
     ns = L.fa_decode_paged_num_splits(ctypes.byref(a))
     assert 1 <= ns <= 64 * 64 // 4
-    bad = decode_args(head_dim=64)
+    bad = decode_args(head_dim=96)
     assert L.fa_decode_paged_workspace_size(ctypes.byref(bad)) == 0
     assert L.fa_decode_paged_num_splits(ctypes.byref(bad)) == 0
 

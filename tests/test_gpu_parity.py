@@ -197,6 +197,40 @@ def test_closed_forms_on_gpu(gpu, dtype):
     assert np.abs(host(o)[0] - mean).max() <= TOL[dtype][0]
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefix_property_on_gpu(gpu, d):
+    """Causal row i equals non-causal attention of query i over keys 0..i
+    (a separate call with seqlen_k = i + 1)."""
+    N, H = 300, 2
+    case = inputs.dense_case(40 + d, 1, N, N, H, H, d, dtype="bf16")
+    q, k, v = (dev(case[n], "bf16") for n in ("q", "k", "v"))
+    o, lse = gpu.fa_fwd(q, k, v, causal=True)
+    for i in (0, 1, 31, 63, 64, 127, 128, 255, 256, 299):
+        oi, li = gpu.fa_fwd(q[:, i:i + 1].contiguous(), k[:, :i + 1].contiguous(), v[:, :i + 1].contiguous(),
+                            causal=False)
+        torch.cuda.synchronize()
+        assert (o[:, i:i + 1].float() - oi.float()).abs().max().item() <= TOL["bf16"][0], i
+        assert (lse[:, :, i:i + 1] - li).abs().max().item() <= 1e-4, i
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_identity_values_give_softmax_rows(gpu, d):
+    """V = identity (N_k = d keys): O row i is the weight row P_i, which sums
+    to one and matches the oracle's weights."""
+    N, H = d, 2
+    case = inputs.dense_case(60 + d, 1, N, N, H, H, d, dtype="bf16")
+    eye = np.zeros((1, N, H, d), np.float32)
+    eye[0, np.arange(N), :, np.arange(N)] = 1.0
+    v = inputs.f32_to_bf16(eye)
+    for causal in (False, True):
+        o, _ = gpu.fa_fwd(dev(case["q"], "bf16"), dev(case["k"], "bf16"), dev(v, "bf16"), causal=causal)
+        torch.cuda.synchronize()
+        og = host(o)
+        assert np.abs(og.sum(-1) - 1.0).max() <= 2e-2
+        o_ref, _ = oracle.dense(case["q"], case["k"], v, causal=causal)
+        check(og.transpose(0, 2, 1, 3), None, o_ref, None, "bf16", f"identity d={d} causal={causal}")
+
+
 def test_strided_views(gpu):
     B, N, H, d = 2, 130, 2, 128
     big = inputs.dense_case(8, B, N, N, 2 * H, 2 * H, d, dtype="bf16")
@@ -341,6 +375,40 @@ def test_decode_parity(gpu, group, num_splits):
                                          case["seq_lens"])
     check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
           f"decode group={group} splits={num_splits}")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("group", [1, 4, 16])
+@pytest.mark.parametrize("num_splits", [0, 1, 7])
+def test_decode_head_dims(gpu, d, group, num_splits):
+    lens = [1, 16, 17, 100, 0, 333, 48, 1000]
+    hkv = 2
+    case = inputs.paged_case(340 + group + d, lens, hkv * group, hkv, d, pad_blocks=2)
+    o, lse = decode_gpu(gpu, case, num_splits=num_splits)
+    o_ref, lse_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                         case["seq_lens"])
+    check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+          f"decode d={d} group={group} splits={num_splits}")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_decode_head_dims_paged_equals_contiguous_bitwise(gpu, d):
+    lens = [700, 17, 1024, 33]
+    case = inputs.paged_case(350 + d, lens, 8, 2, d)
+    o1, l1 = decode_gpu(gpu, case, num_splits=0)
+    bt = case["block_table"]
+    order = np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(lens)]).astype(np.int64)
+    idx = torch.from_numpy(order).cuda()
+    kp = dev(case["k_pool"], "bf16")[idx].contiguous()
+    vp = dev(case["v_pool"], "bf16")[idx].contiguous()
+    table = np.full_like(bt, -1)
+    pos = 0
+    for b, L in enumerate(lens):
+        nb = (L + 15) // 16
+        table[b, :nb] = np.arange(pos, pos + nb)
+        pos += nb
+    o2, l2 = decode_gpu(gpu, case, num_splits=0, k_pool=kp, v_pool=vp, table=torch.from_numpy(table).cuda())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 @pytest.mark.parametrize("lens", [[0, 0, 5], [5, 0, 0], [0], [16, 0, 16, 0, 1]])
