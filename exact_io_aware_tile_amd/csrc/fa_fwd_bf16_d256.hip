@@ -18,10 +18,13 @@
 //   * scores S^T[16 keys x 16 rows] = K Q^T on v_mfma_f32_16x16x32_bf16: lane
 //     l supplies key row l%16 and Q row l%16, head dims 32s + 8(l/16) .. +7;
 //     the accumulator leaves lane l with keys 4(l/16) .. +3 of the block for
-//     row l%16 -- exactly the B operand of O^T += V^T P^T on
-//     v_mfma_f32_16x16x16bf16_1k, so the weights stay in their lanes;
-//   * V^T for that product comes from the row-major V tile through
-//     ds_read_b64_tr_b16 (four keys of one head dim per lane);
+//     row l%16;
+//   * O^T += V^T P^T also on v_mfma_f32_16x16x32_bf16 (16x16x16 runs at half
+//     its rate), over both 16-key blocks of a tile: contraction slot
+//     8(l/16) + e is key 4(l/16) + e of block 0 for e < 4 and key
+//     4(l/16) + e - 4 of block 1 otherwise -- exactly the weights lane l holds
+//     for row l%16, so they stay in their lanes; the matching V^T operand is
+//     two ds_read_b64_tr_b16 reads (four keys of one head dim each);
 //   * 32-key tiles: a K or V tile is 16 KB and the two 4-stage rings 128 KB;
 //   * a row's 32 scores of a tile sit in the four lanes l%16 + 16g; the row
 //     max (taken only when the reference must move) and the final sum reduce
@@ -300,9 +303,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     l_run += ps;
   };
 
-  // O^T += V^T P^T over the two 16-key blocks of tile t: lane 4k + q of
-  // group j reads key row 16kc + 4j + k, head dims 16db + 4q .. +3; the
-  // transposed read leaves lane n with dim 16db + n of keys 16kc + 4j .. +3.
+  // O^T += V^T P^T over both 16-key blocks of tile t in one product per
+  // 16 head dims: lane 4k + q of group j reads key rows 4j + k (block 0)
+  // and 16 + 4j + k (block 1), head dims 16db + 4q .. +3; each transposed
+  // read leaves lane n with dim 16db + n of four keys of its block.
   const int tk = n >> 2;
   const int tq = n & 3;
   auto pv = [&](int t) {
@@ -313,21 +317,29 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
         for (int r = 0; r < 4; ++r) oacc[db][r] *= alpha;
     }
     const uint16_t* vs = &v_s[t % kStages][0];
+    const uint2 p0 = __builtin_bit_cast(uint2, pf[0]);
+    const uint2 p1 = __builtin_bit_cast(uint2, pf[1]);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(p0.x, p0.y, p1.x, p1.y));
+    const int va = 4 * j + tk;
+    const int vb = 16 + 4 * j + tk;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int vr = 16 * kc + 4 * j + tk;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)&vs[vr * D + swz_v(vr, 2 * db + (tq >> 1)) * 8 + 4 * (tq & 1)]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pf[kc], oacc[db], 0, 0, 0);
-      }
+    for (int db = 0; db < D / 16; ++db) {
+      const int dc = 2 * db + (tq >> 1);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)&vs[va * D + swz_v(va, dc) * 8 + 4 * (tq & 1)]);
+      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)&vs[vb * D + swz_v(vb, dc) * 8 + 4 * (tq & 1)]);
+      const uint2 l2 = __builtin_bit_cast(uint2, lo);
+      const uint2 u2 = __builtin_bit_cast(uint2, up);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, u2.x, u2.y)), pb, oacc[db], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, kVAhead, 0);
+    // Two transposed reads per MFMA; kVAhead MFMAs' worth in flight.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
 #pragma unroll
-    for (int i = 0; i < D / 8 - kVAhead; ++i) {
+    for (int i = 0; i < D / 16 - kVAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
   };
