@@ -307,8 +307,8 @@ FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
   if (a->heads_q % a->heads_kv)
     return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
                 a->heads_kv);
-  if (a->head_dim != 64 && a->head_dim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: head_dim %d, supported 64 and 128", a->head_dim);
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: head_dim %d, supported 64, 128 and 256", a->head_dim);
   if (a->block_size != fa::kFwdPagedBlock)
     return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: block_size %d, supported %d", a->block_size,
                 fa::kFwdPagedBlock);
@@ -329,7 +329,7 @@ FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
   if (a->pool_stride[2] > fa::kFwdMaxKvRowStrideBf16)
     return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: pool token stride above %lld elements",
                 (long long)fa::kFwdMaxKvRowStrideBf16);
-  const int64_t rows = fa::kFwdRowsPerTileBf16;
+  const int64_t rows = fa::fwd_rows_per_tile_bf16(a->head_dim);
   const int64_t qtiles = (a->max_seqlen_q + rows - 1) / rows;
   if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
     return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: grid too large");

@@ -1,5 +1,6 @@
 // fa_fwd_bf16_d256.hip -- bf16 prefill attention at head_dim 256 on gfx950
-// (dense and packed sequences, optional dropout).
+// (dense and packed sequences, optional dropout; chunked prefill over a
+// paged KV pool).
 //
 // Method: the online-softmax recurrence of "S12 FlashAttention"
 // (llminference.xinbetween.com), "Core idea / The solution" and "Mechanics /
@@ -28,7 +29,11 @@
 //   * 32-key tiles: a K or V tile is 16 KB and the two 4-stage rings 128 KB;
 //   * a row's 32 scores of a tile sit in the four lanes l%16 + 16g; the row
 //     max (taken only when the reference must move) and the final sum reduce
-//     over those four lanes.
+//     over those four lanes;
+//   * paged pools: a 32-key tile is two 16-token pool blocks and each wave of
+//     the loading group covers 8 rows, half a block; only its DMA base
+//     changes, to the pool block the table names ("S12 FlashAttention",
+//     "What this unlocks beyond speed": tiles fetched through a block table).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -72,8 +77,9 @@ __device__ __forceinline__ f32x4 zero4() {
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ (2 * (r & 7)); }
 
-template <bool CAUSAL, bool DROP>
+template <bool CAUSAL, bool PAGED, bool DROP>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams p) {
+  static_assert(!(PAGED && DROP), "dropout is built for dense and packed prefill");
   __shared__ __attribute__((aligned(1024))) uint16_t k_s[kStages][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_s[kStages][TILE];
 
@@ -104,7 +110,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
 
   int nq, nk;
   int64_t q_base, k_base, v_base, o_base, lse_base;
-  if (p.cu_seqlens) {
+  if (PAGED) {
+    // new queries packed by cu_seqlens; keys of the sequence in the pools
+    const int s0 = p.cu_seqlens[b];
+    nq = p.cu_seqlens[b + 1] - s0;
+    nk = min(max(p.seq_lens_k[b], 0), p.seqlen_k);
+    q_base = (int64_t)s0 * p.q_ss;
+    k_base = 0;
+    v_base = 0;
+    o_base = (int64_t)s0 * p.o_ss;
+    lse_base = (int64_t)h * p.total_tokens + s0;
+  } else if (p.cu_seqlens) {
     const int s0 = p.cu_seqlens[b];
     const int s1 = p.cu_seqlens[b + 1];
     nq = nk = s1 - s0;
@@ -126,8 +142,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   if (q0 >= nq) return;  // uniform over the workgroup
   const int g = h / p.group;
   q_base += (int64_t)h * p.q_hs;
-  k_base += (int64_t)g * p.k_hs;
-  v_base += (int64_t)g * p.v_hs;
+  k_base += (int64_t)g * (PAGED ? p.p_hs : p.k_hs);
+  v_base += (int64_t)g * (PAGED ? p.p_hs : p.v_hs);
   o_base += (int64_t)h * p.o_hs;
   const int off = nk - nq;  // causal: key i visible from row r iff i <= r + off
 
@@ -167,32 +183,66 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   const int drow = lane / CH;
   const int dpch = lane % CH;
   const int wq = wave & 3;
+  // Paged: wave w's rows 8(w%4) .. +7 of a tile are half of pool block
+  // 2t + (w%4)/2 (rows (w%4 odd) 8 .. 15 or 0 .. 7 of it); the lane offsets
+  // are then relative to that block.
+  const int64_t kv_row_k = PAGED ? p.p_ts : p.k_ss;
+  const int64_t kv_row_v = PAGED ? p.p_ts : p.v_ss;
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = wq * RPW + i * RPI + drow;
-    koff[i] = (uint32_t)(((int64_t)r * p.k_ss + swz_k(r, dpch) * 8) * 2);
-    voff[i] = (uint32_t)(((int64_t)r * p.v_ss + swz_v(r, dpch) * 8) * 2);
+    const int r = wq * RPW + i * RPI + drow;  // row of the tile in LDS
+    const int rs = PAGED ? r & (kFwdPagedBlock - 1) : r;  // ... in the source
+    koff[i] = (uint32_t)(((int64_t)rs * kv_row_k + swz_k(r, dpch) * 8) * 2);
+    voff[i] = (uint32_t)(((int64_t)rs * kv_row_v + swz_v(r, dpch) * 8) * 2);
   }
-  auto dma_one = [&](int tile, bool v_op, int i) {
+  // Paged: the block holding the wave's rows of tile `tile` (a block past
+  // the last key is replaced by the last key's block), and its pool block,
+  // read through the scalar cache as in the head_dim 64 / 128 kernel.
+  auto wave_block = [&](int tile) {
+    return __builtin_amdgcn_readfirstlane(
+        min(tile * (kBc / kFwdPagedBlock) + wq * RPW / kFwdPagedBlock, (nk - 1) / kFwdPagedBlock));
+  };
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (PAGED ? (int64_t)b * p.max_blocks : 0));
+  auto pool_block = [&](int tile) -> int32_t {
+    if (!PAGED || tile < 0) return 0;
+    return table[wave_block(tile)];
+  };
+  auto dma_one = [&](int tile, bool v_op, int i, int32_t phys) {
     const int st = tile % kStages;
     const int r0 = wq * RPW + i * RPI;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
     const int rows_left = nk - tile * kBc;  // uniform
-    const uint16_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
     uint32_t o = v_op ? voff[i] : koff[i];
-    if (rows_left < kBc) {
-      const int r = r0 + drow;
-      const int rk = min(r, rows_left - 1);
-      o = v_op ? (uint32_t)(((int64_t)rk * p.v_ss + swz_v(r, dpch) * 8) * 2)
-               : (uint32_t)(((int64_t)rk * p.k_ss + swz_k(r, dpch) * 8) * 2);
+    if (PAGED) {
+      // In the last tile rows past the last key re-read that key, in the
+      // last key's block.
+      if (rows_left < kBc) {
+        const int r = r0 + drow;
+        const int key = tile * kBc + min(r, rows_left - 1);
+        const int rb = key - wave_block(tile) * kFwdPagedBlock;
+        o = v_op ? (uint32_t)(((int64_t)rb * p.p_ts + swz_v(r, dpch) * 8) * 2)
+                 : (uint32_t)(((int64_t)rb * p.p_ts + swz_k(r, dpch) * 8) * 2);
+      }
+      const uint16_t* base = (v_op ? vg : kg) + (int64_t)phys * p.p_bs;
+      dma_16b(base, o, lds);
+    } else {
+      const uint16_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
+      if (rows_left < kBc) {
+        const int r = r0 + drow;
+        const int rk = min(r, rows_left - 1);
+        o = v_op ? (uint32_t)(((int64_t)rk * p.v_ss + swz_v(r, dpch) * 8) * 2)
+                 : (uint32_t)(((int64_t)rk * p.k_ss + swz_k(r, dpch) * 8) * 2);
+      }
+      dma_16b(base, o, lds);
     }
-    dma_16b(base, o, lds);
   };
   auto dma_op = [&](int tile, bool v_op) {
+    const int32_t phys = pool_block(tile);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i);
+    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i, phys);
   };
 
   if (nt > 0) dma_op(0, grp != 0);
@@ -229,14 +279,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   const uint32_t tm1 = DROP ? (uint32_t)(p.drop_t - 1) * 0x00010001u : 0u;
   bool corr = false;
   float alpha = 1.f;
-  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v) {
+  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v, int32_t dma_phys) {
     float ps2[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (dma_tile >= 0) {
         __builtin_amdgcn_sched_barrier(0);
-        dma_one(dma_tile, dma_v, 2 * kb);
-        dma_one(dma_tile, dma_v, 2 * kb + 1);
+        dma_one(dma_tile, dma_v, 2 * kb, dma_phys);
+        dma_one(dma_tile, dma_v, 2 * kb + 1, dma_phys);
         __builtin_amdgcn_sched_barrier(0);
       }
       float pv[4];
@@ -256,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     ps = ps2[0] + ps2[1];
   };
 
-  auto softmax = [&](int t, int dma_tile, bool dma_v) {
+  auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
     if (need_mask) {
@@ -287,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     // kernel): a lane partial sum above the bound, infinite or NaN sends the
     // wave to the exact step.
     float ps;
-    weights(m_run, ps, dma_tile, dma_v);
+    weights(m_run, ps, dma_tile, dma_v, dma_phys);
     corr = __any(!(ps <= kLazyBound));
     if (corr) {
       float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
@@ -298,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false, 0);
     }
     l_run += ps;
   };
@@ -366,33 +416,40 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     wait_vmcnt<0>();
     if (nt > 1) dma_op(1, grp != 0);
     lds_barrier();
+    // Paged: the table entry for the DMA of the next softmax phase is read
+    // at the end of the MFMA phase before it (see the head_dim 64 / 128
+    // kernel).
     if (grp == 0) {
       scores(0);
+      int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 2 < nt ? t + 2 : -1, true);
+        softmax(t, t + 2 < nt ? t + 2 : -1, true, ph);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
+        ph = pool_block(t + 3 < nt ? t + 3 : -1);
         phase_end(2 * t + 2);
       }
       phase_end(2 * nt + 1);
     } else {
       if (2 < nt) dma_op(2, false);
+      int32_t ph = pool_block(3 < nt ? 3 : -1);
       phase_end(0);
       scores(0);
       phase_end(1);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 3 < nt ? t + 3 : -1, false);
+        softmax(t, t + 3 < nt ? t + 3 : -1, false, ph);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
+        ph = pool_block(t + 4 < nt ? t + 4 : -1);
         phase_end(2 * t + 3);
       }
     }
@@ -431,17 +488,21 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
 template <bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int64_t nwg = (int64_t)p.num_qtiles * p.heads_q * p.batch;
-  if (p.drop_t > 0)
-    hipLaunchKernelGGL((fwd_bf16_d256_kernel<CAUSAL, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  if (p.paged)
+    hipLaunchKernelGGL((fwd_bf16_d256_kernel<CAUSAL, true, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
+  else if (p.drop_t > 0)
+    hipLaunchKernelGGL((fwd_bf16_d256_kernel<CAUSAL, false, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((fwd_bf16_d256_kernel<CAUSAL, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_d256_kernel<CAUSAL, false, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16_d256(const FwdParams& p, hipStream_t stream) {
-  if (p.paged) return hipErrorInvalidValue;
   return p.causal ? launch<true>(p, stream) : launch<false>(p, stream);
 }
 

@@ -234,7 +234,7 @@ fa_status fa_fwd_varlen_dropout(const fa_fwd_varlen_args *args, const fa_dropout
  * keys j <= i + n_k - n_q: the chunk is the last n_q positions of the
  * sequence.  A query that sees no key (a chunk longer than its keys, or
  * n_k = 0) gets o = 0 and lse = -inf.  A chunk of one query is a decode
- * step.  Supported: bf16, head_dim 64 or 128, block_size 16.
+ * step.  Supported: bf16, head_dim 64, 128 or 256, block_size 16.
  */
 typedef struct {
   const void *q;

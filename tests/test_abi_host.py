@@ -277,7 +277,6 @@ def paged_args(**kw):
     (dict(heads_q=7), fa.FA_ERR_BAD_SHAPE),
     (dict(total_q=-1), fa.FA_ERR_BAD_SHAPE),
     (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(head_dim=256), fa.FA_ERR_UNSUPPORTED),
     (dict(block_size=32), fa.FA_ERR_UNSUPPORTED),
     (dict(max_seqlen_k=20 * 16 + 1), fa.FA_ERR_BAD_SHAPE),
     (dict(scale=-1.0), fa.FA_ERR_BAD_SHAPE),

@@ -504,7 +504,7 @@ PAGED_K = [1, 333, 7, 0, 1000, 300, 4, 600, 40]
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("group", [1, 4])
 def test_paged_prefill_parity(gpu, group, d, causal):
     case = inputs.paged_prefill_case(400 + 10 * group + d, PAGED_Q, PAGED_K, 2 * group, 2, d, pad_blocks=1)
@@ -512,11 +512,12 @@ def test_paged_prefill_parity(gpu, group, d, causal):
     check(og, lg, o_ref, lse_ref, "bf16", f"paged prefill group={group} d={d} causal={causal}")
 
 
-def test_paged_prefill_whole_context_is_varlen_bitwise(gpu):
+@pytest.mark.parametrize("d", [128, 256])
+def test_paged_prefill_whole_context_is_varlen_bitwise(gpu, d):
     # a chunk that is the whole context reads exactly the keys the packed
     # kernel reads, in the same tiles: identical bits
     lens = [300, 64, 17, 700]
-    case = inputs.paged_prefill_case(410, lens, lens, 8, 2, 128)
+    case = inputs.paged_prefill_case(410 + d, lens, lens, 8, 2, d)
     o1, l1 = paged_prefill_gpu(gpu, case, causal=True)
     bs = case["block_size"]
     kp, vp = dev(case["k_pool"], "bf16"), dev(case["v_pool"], "bf16")
@@ -534,9 +535,10 @@ def test_paged_prefill_whole_context_is_varlen_bitwise(gpu):
     assert torch.equal(l1, l2)
 
 
-def test_paged_prefill_pool_order_bitwise(gpu):
+@pytest.mark.parametrize("d", [128, 256])
+def test_paged_prefill_pool_order_bitwise(gpu, d):
     q_lens, k_lens = [512, 33, 200], [2000, 33, 1500]
-    case = inputs.paged_prefill_case(420, q_lens, k_lens, 16, 4, 128)
+    case = inputs.paged_prefill_case(420 + d, q_lens, k_lens, 16, 4, d)
     o1, l1 = paged_prefill_gpu(gpu, case)
     bt = case["block_table"]
     order = np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(k_lens)]).astype(np.int64)
