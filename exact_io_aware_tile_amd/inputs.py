@@ -195,6 +195,17 @@ def varlen_case(seed: int, lengths, hq: int, hkv: int, d: int, dtype: str = "bf1
     }
 
 
+def fp8_varlen_case(seed: int, lengths, hq: int, hkv: int, d: int) -> dict:
+    """Packed case in FP8 E4M3 with per-tensor descale factors (the same
+    float32 draws as ``varlen_case``)."""
+    c = varlen_case(seed, lengths, hq, hkv, d, dtype="f32")
+    q8, qd = to_fp8(c["q"])
+    k8, kd = to_fp8(c["k"])
+    v8, vd = to_fp8(c["v"])
+    c.update(q=q8, k=k8, v=v8, descale=(qd, kd, vd), dtype="fp8")
+    return c
+
+
 # --------------------------------------------------------------------------
 # paged decode: q [B, Hq, d]; pools [num_blocks, Hkv, block, d]; table [B, max_blocks]
 # --------------------------------------------------------------------------

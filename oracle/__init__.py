@@ -264,6 +264,18 @@ def fp8_dense(q8, k8, v8, descale, *, causal: bool, scale: float | None = None, 
     return dense(q, k, v, causal=causal, scale=scale, rows=rows, nthreads=nthreads, lib=lib)
 
 
+def fp8_varlen(q8, k8, v8, cu_seqlens, descale, *, causal: bool, scale: float | None = None, rows=None,
+               nthreads: int = 0, lib=None):
+    """Packed attention over FP8 E4M3 inputs with per-tensor descale factors:
+    ``varlen`` on descale[i] * value(code), with the layouts and return values
+    of ``varlen``."""
+    qd, kd, vd = (float(x) for x in descale)
+    q = decode_e4m3(q8, lib=lib) * qd
+    k = decode_e4m3(k8, lib=lib) * kd
+    v = decode_e4m3(v8, lib=lib) * vd
+    return varlen(q, k, v, cu_seqlens, causal=causal, scale=scale, rows=rows, nthreads=nthreads, lib=lib)
+
+
 def dropout_threshold(p: float) -> int:
     """Byte threshold t of a dropout probability: t = rint(256 p), p in [0, 1)
     with t <= 255; a weight is kept iff its random byte >= t, with probability

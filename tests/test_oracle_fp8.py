@@ -63,6 +63,21 @@ def test_fp8_dense_equals_dense_on_widened_inputs():
         np.testing.assert_array_equal(lse, l2)
 
 
+def test_fp8_varlen_equals_fp8_dense_per_sequence():
+    lens = [5, 0, 23, 1]
+    c = inputs.fp8_varlen_case(72, lens, 4, 2, 16)
+    cu, ds = c["cu_seqlens"], tuple(float(x) for x in c["descale"])
+    for causal in (False, True):
+        o, lse = oracle.fp8_varlen(c["q"], c["k"], c["v"], cu, ds, causal=causal)
+        for s, L in enumerate(lens):
+            if L == 0:
+                continue
+            a, b = cu[s], cu[s + 1]
+            od, ld = oracle.fp8_dense(c["q"][None, a:b], c["k"][None, a:b], c["v"][None, a:b], ds, causal=causal)
+            np.testing.assert_array_equal(o[:, a:b], od[0])
+            np.testing.assert_array_equal(lse[:, a:b], ld[0])
+
+
 def test_v_descale_scales_output_only():
     q8, k8, v8, (qd, kd, vd) = _case(72)
     o1, l1 = oracle.fp8_dense(q8, k8, v8, (qd, kd, vd), causal=True)
