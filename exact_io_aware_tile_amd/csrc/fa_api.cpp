@@ -299,6 +299,61 @@ FA_EXPORT fa_status fa_fwd_fp8(const fa_fwd_fp8_args* a, void* stream) {
   return ok();
 }
 
+FA_EXPORT fa_status fa_fwd_varlen_fp8(const fa_fwd_varlen_fp8_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen_fp8: args is NULL");
+  if (a->num_seqs < 0 || a->total_tokens < 0 || a->max_seqlen < 0 || a->heads_q <= 0 || a->heads_kv <= 0)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen_fp8: negative or zero size");
+  if (a->heads_q % a->heads_kv)
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen_fp8: heads_q (%d) is not a multiple of heads_kv (%d)",
+                a->heads_q, a->heads_kv);
+  if (a->head_dim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen_fp8: head_dim %d, supported 128", a->head_dim);
+  if (!(a->scale > 0.f) || !std::isfinite(a->scale))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen_fp8: scale must be positive and finite");
+  for (float d : {a->q_descale, a->k_descale, a->v_descale})
+    if (!(d > 0.f) || !std::isfinite(d))
+      return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen_fp8: descale factors must be positive and finite");
+  if (a->num_seqs == 0 || a->max_seqlen == 0 || a->total_tokens == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->o || !a->cu_seqlens)
+    return fail(FA_ERR_NULL_POINTER, "fa_fwd_varlen_fp8: q, k, v, o and cu_seqlens are required");
+  if (!strides_ok(a->q_stride, 2, 16) || !strides_ok(a->k_stride, 2, 16) || !strides_ok(a->v_stride, 2, 16) ||
+      !strides_ok(a->o_stride, 2, 8))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen_fp8: strides must be non-negative multiples of 16 bytes");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_varlen_fp8: q, k, v, o must be 16-byte aligned");
+  if (a->k_stride[0] > fa::kFwdMaxKvRowStrideBf16 || a->v_stride[0] > fa::kFwdMaxKvRowStrideBf16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen_fp8: k/v token strides above %lld elements",
+                (long long)fa::kFwdMaxKvRowStrideBf16);
+  const int64_t qtiles = (a->max_seqlen + fa::kFwdRowsPerTileFp8 - 1) / fa::kFwdRowsPerTileFp8;
+  if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_varlen_fp8: grid too large");
+
+  fa::FwdParams p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.cu_seqlens = a->cu_seqlens;
+  p.q_bs = 0, p.q_ss = a->q_stride[0], p.q_hs = a->q_stride[1];
+  p.k_bs = 0, p.k_ss = a->k_stride[0], p.k_hs = a->k_stride[1];
+  p.v_bs = 0, p.v_ss = a->v_stride[0], p.v_hs = a->v_stride[1];
+  p.o_bs = 0, p.o_ss = a->o_stride[0], p.o_hs = a->o_stride[1];
+  p.batch = a->num_seqs;
+  p.seqlen_q = a->max_seqlen;
+  p.seqlen_k = a->max_seqlen;
+  p.total_tokens = a->total_tokens;
+  p.heads_q = a->heads_q;
+  p.group = a->heads_q / a->heads_kv;
+  p.num_qtiles = (int32_t)qtiles;
+  p.causal = a->causal ? 1 : 0;
+  p.scale_log2 = (float)((double)a->scale * a->q_descale * a->k_descale * 1.4426950408889634073599);
+  p.o_scale = a->v_descale;
+  const hipError_t e = fa::launch_fwd_fp8(p, a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_varlen_fp8: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
   if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: args is NULL");
   if (a->num_seqs < 0 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0 || a->heads_q <= 0 ||

@@ -9,6 +9,7 @@ Layouts (see include/fa.h):
     fa_fwd:          q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> o like q, lse [B, Hq, Nq]
     fa_fwd_fp8:      as fa_fwd with uint8 E4M3 q/k/v and per-tensor descale factors -> o bf16
     fa_fwd_varlen:   q [T, Hq, d], k/v [T, Hkv, d], cu_seqlens int32 [S+1] -> o, lse [Hq, T]
+    fa_fwd_varlen_fp8: as fa_fwd_varlen with uint8 E4M3 q/k/v and descale factors -> o bf16
     fa_fwd_dropout, fa_fwd_varlen_dropout: as fa_fwd / fa_fwd_varlen (bf16) with dropout
                      of the weights drawn from (dropout_p, seed, offset)
     fa_fwd_paged:    q [Tq, Hq, d] (chunks packed by cu_seqlens_q int32 [S+1]), pools and
@@ -59,6 +60,15 @@ class FwdVarlenArgs(ctypes.Structure):
                 ("dtype", ctypes.c_int), ("scale", _F), ("causal", _I32)]
 
 
+class FwdVarlenFp8Args(ctypes.Structure):
+    _fields_ = [("q", _P), ("k", _P), ("v", _P), ("o", _P), ("lse", _P), ("cu_seqlens", _P),
+                ("num_seqs", _I32), ("total_tokens", _I32), ("max_seqlen", _I32), ("heads_q", _I32),
+                ("heads_kv", _I32), ("head_dim", _I32),
+                ("q_stride", _I64 * 2), ("k_stride", _I64 * 2), ("v_stride", _I64 * 2),
+                ("o_stride", _I64 * 2),
+                ("q_descale", _F), ("k_descale", _F), ("v_descale", _F), ("scale", _F), ("causal", _I32)]
+
+
 class DropoutArgs(ctypes.Structure):
     _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint32)]
 
@@ -82,7 +92,7 @@ class FwdPagedArgs(ctypes.Structure):
                 ("max_blocks_per_seq", _I32), ("num_blocks", _I32), ("scale", _F), ("causal", _I32)]
 
 
-SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
+SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_fp8", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
@@ -108,6 +118,8 @@ def lib(path: str = LIB_PATH):
     L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_fwd_varlen.argtypes = [ctypes.POINTER(FwdVarlenArgs), _P]
     L.fa_fwd_varlen.restype = ctypes.c_int
+    L.fa_fwd_varlen_fp8.argtypes = [ctypes.POINTER(FwdVarlenFp8Args), _P]
+    L.fa_fwd_varlen_fp8.restype = ctypes.c_int
     L.fa_fwd_dropout.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(DropoutArgs), _P]
     L.fa_fwd_dropout.restype = ctypes.c_int
     L.fa_fwd_varlen_dropout.argtypes = [ctypes.POINTER(FwdVarlenArgs), ctypes.POINTER(DropoutArgs), _P]
@@ -286,6 +298,37 @@ def _varlen_args(q, k, v, cu_seqlens, max_seqlen, causal, scale, out, lse, retur
     a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     a.causal = int(bool(causal))
     return a, out, lse
+
+
+def fa_fwd_varlen_fp8(q, k, v, cu_seqlens, max_seqlen: int, descale, *, causal: bool = True,
+                      scale: float | None = None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Packed attention over FP8 E4M3 codes (uint8 q [T, Hq, d], k/v [T, Hkv, d])
+    standing for descale[i] * value(code).  Returns (o, lse), o in bf16."""
+    torch = _torch()
+    _dev(q, k, v, out, lse, cu_seqlens)
+    for t in (q, k, v):
+        if t.dtype != torch.uint8:
+            raise TypeError("fa_fwd_varlen_fp8 takes E4M3 codes as uint8 tensors")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    a = FwdVarlenFp8Args()
+    a.q, a.k, a.v, a.o, a.lse = _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.num_seqs, a.total_tokens, a.max_seqlen = cu_seqlens.numel() - 1, T, int(max_seqlen)
+    a.heads_q, a.heads_kv, a.head_dim = Hq, Hkv, d
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", out)):
+        getattr(a, name)[:] = list(t.stride()[:2])
+    a.q_descale, a.k_descale, a.v_descale = (float(x) for x in descale)
+    a.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    a.causal = int(bool(causal))
+    _check(lib().fa_fwd_varlen_fp8(ctypes.byref(a), _stream(stream)))
+    return out, lse
 
 
 def _fwd_paged_args(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_OK = 0,
@@ -167,6 +167,33 @@ typedef struct {
 } fa_fwd_varlen_args;
 
 fa_status fa_fwd_varlen(const fa_fwd_varlen_args *args, void *stream);
+
+/*
+ * fa_fwd_varlen_fp8 -- packed variable-length sequences (as fa_fwd_varlen)
+ * over FP8 E4M3 inputs with per-tensor descale factors (as fa_fwd_fp8).
+ *
+ *   q  [total_tokens, heads_q,  head_dim] E4M3 codes, strides q_stride = {token, head}
+ *   k,v[total_tokens, heads_kv, head_dim] E4M3
+ *   o  [total_tokens, heads_q,  head_dim] bf16 (written)
+ *   lse [heads_q, total_tokens] fp32 contiguous (written; may be NULL)
+ *   cu_seqlens, max_seqlen: as for fa_fwd_varlen.
+ *
+ * Arithmetic, rounding, head_dim (128), stride and descale rules are those
+ * of fa_fwd_fp8; sequence rules those of fa_fwd_varlen.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int32_t *cu_seqlens;
+  int32_t num_seqs, total_tokens, max_seqlen, heads_q, heads_kv, head_dim;
+  int64_t q_stride[2], k_stride[2], v_stride[2], o_stride[2];
+  float q_descale, k_descale, v_descale;
+  float scale;
+  int32_t causal;
+} fa_fwd_varlen_fp8_args;
+
+fa_status fa_fwd_varlen_fp8(const fa_fwd_varlen_fp8_args *args, void *stream);
 
 /*
  * fa_fwd_dropout / fa_fwd_varlen_dropout -- fa_fwd and fa_fwd_varlen with

@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 5
+    assert L.fa_abi_version() == declared == 6
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -69,6 +69,7 @@ STRUCTS = {
     "fa_fwd_fp8_args": fa.FwdFp8Args,
     "fa_decode_paged_args": fa.DecodePagedArgs,
     "fa_dropout_args": fa.DropoutArgs,
+    "fa_fwd_varlen_fp8_args": fa.FwdVarlenFp8Args,
 }
 
 
@@ -216,6 +217,46 @@ def test_dropout_null_and_noop(L):
     # p rounding to t = 0 is plain attention, allowed for fp32 too
     e = fwd_args(q=None, k=None, v=None, o=None, batch=0, dtype=fa.FA_F32)
     assert L.fa_fwd_dropout(ctypes.byref(e), ctypes.byref(dropout_args(p=0.5 / 256)), None) == fa.FA_OK
+
+
+def varlen_fp8_args(**kw):
+    a = fa.FwdVarlenFp8Args()
+    a.num_seqs, a.total_tokens, a.max_seqlen, a.heads_q, a.heads_kv, a.head_dim = 2, 10, 6, 2, 1, 128
+    a.q_descale = a.k_descale = a.v_descale = 0.01
+    a.scale, a.causal = 0.088, 1
+    a.q = a.k = a.v = a.o = a.cu_seqlens = 0x1000
+    a.q_stride[:] = [2 * 128, 128]
+    a.o_stride[:] = [2 * 128, 128]
+    a.k_stride[:] = a.v_stride[:] = [128, 128]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(a, k)[:] = v
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=3, heads_kv=2), fa.FA_ERR_BAD_SHAPE),
+    (dict(num_seqs=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(k_descale=0.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(v_descale=float("nan")), fa.FA_ERR_BAD_SHAPE),
+    (dict(cu_seqlens=None), fa.FA_ERR_NULL_POINTER),
+    (dict(q_stride=[264, 8]), fa.FA_ERR_BAD_SHAPE),
+    (dict(o=0x1008), fa.FA_ERR_BAD_SHAPE),
+    (dict(k_stride=[(1 << 24) + 16, 128]), fa.FA_ERR_UNSUPPORTED),
+])
+def test_varlen_fp8_rejects_before_launch(L, kw, status):
+    a = varlen_fp8_args(**kw)
+    assert L.fa_fwd_varlen_fp8(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_varlen_fp8_empty_is_noop(L):
+    for kw in (dict(num_seqs=0), dict(max_seqlen=0), dict(total_tokens=0)):
+        a = varlen_fp8_args(q=None, k=None, v=None, o=None, cu_seqlens=None, **kw)
+        assert L.fa_fwd_varlen_fp8(ctypes.byref(a), None) == fa.FA_OK
 
 
 def varlen_args(**kw):

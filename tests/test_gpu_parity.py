@@ -618,6 +618,32 @@ def check_fp8(og, lg, o_ref, lse_ref, what):
         assert e <= LSE_TOL, f"{what}: max |dLSE| = {e:.3e}"
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_varlen_parity(gpu, causal):
+    lens = [1, 130, 0, 64, 257, 7, 128, 300]
+    case = inputs.fp8_varlen_case(610, lens, 4, 2, 128)
+    q, k, v = (torch.from_numpy(case[n]).cuda() for n in ("q", "k", "v"))
+    cu = torch.from_numpy(case["cu_seqlens"]).cuda()
+    o, lse = gpu.fa_fwd_varlen_fp8(q, k, v, cu, case["max_seqlen"], case["descale"], causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fp8_varlen(case["q"], case["k"], case["v"], case["cu_seqlens"], case["descale"],
+                                       causal=causal)
+    check_fp8(host(o).transpose(1, 0, 2), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
+              f"fp8 varlen causal={causal}")
+
+
+def test_fp8_varlen_single_sequence_equals_dense_bitwise(gpu):
+    N = 700
+    case = inputs.fp8_case(611, 1, N, N, 3, 3, 128)
+    q, k, v = (torch.from_numpy(case[n]).cuda() for n in ("q", "k", "v"))
+    od, ld = gpu.fa_fwd_fp8(q, k, v, case["descale"], causal=True)
+    cu = torch.tensor([0, N], dtype=torch.int32).cuda()
+    ov, lv = gpu.fa_fwd_varlen_fp8(q[0], k[0], v[0], cu, N, case["descale"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(od[0], ov)
+    assert torch.equal(ld[0], lv)
+
+
 FP8_SHAPES = [
     # B, Nq, Nk, Hq, Hkv
     (1, 1, 1, 1, 1),
