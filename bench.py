@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "fp8": ["exact_io_aware_tile_amd/csrc/fa_fwd_fp8.hip"],
     "dropout": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "d256": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16_d256.hip"],
+    "varlen": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "decode_d256": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
 }
 
@@ -224,7 +225,7 @@ def run_varlen(fa, case, steps, warmup, torch, np):
     return {"ms": ms, "tflops": tf, "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": measured_traffic("varlen")}}
 
 
 def run_paged_prefill(fa, case, steps, warmup, torch, np):
