@@ -245,6 +245,73 @@ def test_strided_views(gpu):
           "strided")
 
 
+def _spread_rows(src, row_stride, fill=float("nan")):
+    """Device copy of a contiguous [1, N, 1, d] tensor whose rows lie row_stride
+    elements apart in one buffer filled with FILL elsewhere (a stray read of
+    the gaps shows up as a non-finite output)."""
+    _, N, _, d = src.shape
+    buf = torch.full(((N - 1) * row_stride + d,), fill, dtype=src.dtype, device="cuda")
+    view = buf.as_strided((1, N, 1, d), (0, row_stride, d, 1))
+    view.copy_(src)
+    return view
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_max_kv_row_stride(gpu, d):
+    """k/v rows 2^24 elements apart (the largest stride the bf16 kernels'
+    32-bit lane offsets accept), over several tiles and a ragged tail."""
+    N = 100
+    case = inputs.dense_case(70 + d, 1, N, N, 1, 1, d, dtype="bf16")
+    q = dev(case["q"], "bf16")
+    k = _spread_rows(dev(case["k"], "bf16"), 1 << 24)
+    v = _spread_rows(dev(case["v"], "bf16"), 1 << 24)
+    for causal in (False, True):
+        o, lse = gpu.fa_fwd(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.dense(case["q"], case["k"], case["v"], causal=causal)
+        check(host(o).transpose(0, 2, 1, 3), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+              f"k/v row stride 2^24 d={d} causal={causal}")
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_max_kv_row_stride_fp8(gpu):
+    N = 100
+    case = inputs.fp8_case(75, 1, N, N, 1, 1, 128)
+    q = torch.from_numpy(case["q"]).cuda()
+    k = _spread_rows(torch.from_numpy(case["k"]).cuda(), 1 << 24, fill=0x7F)  # 0x7F: E4M3 NaN
+    v = _spread_rows(torch.from_numpy(case["v"]).cuda(), 1 << 24, fill=0x7F)
+    o, lse = gpu.fa_fwd_fp8(q, k, v, case["descale"], causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fp8_dense(case["q"], case["k"], case["v"], case["descale"], causal=True)
+    check_fp8(host(o).transpose(0, 2, 1, 3), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
+              "fp8 k/v row stride 2^24")
+    del k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_decode_max_token_stride(gpu, d):
+    """Pool tokens 2^26 elements apart (the largest token stride the decode
+    kernel's 32-bit lane offsets accept), two sequences over two blocks."""
+    lens = [20, 9]
+    case = inputs.paged_case(80 + d, lens, 2, 1, d)
+    nb = case["k_pool"].shape[0]
+    ts = 1 << 26
+    def spread(a):
+        buf = torch.full(((nb * 16 - 1) * ts + d,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        view = buf.as_strided((nb, 1, 16, d), (16 * ts, 16 * ts, ts, 1))
+        view.copy_(dev(a, "bf16"))
+        return view
+    kp, vp = spread(case["k_pool"]), spread(case["v_pool"])
+    o, lse = decode_gpu(gpu, case, k_pool=kp, v_pool=vp)
+    o_ref, lse_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                         case["seq_lens"])
+    check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16", f"decode token stride 2^26 d={d}")
+    del kp, vp
+    torch.cuda.empty_cache()
+
+
 def test_empty_keys(gpu):
     q = torch.randn(1, 5, 2, 64, device="cuda").to(torch.bfloat16)
     k = torch.zeros(1, 0, 2, 64, device="cuda", dtype=torch.bfloat16)
