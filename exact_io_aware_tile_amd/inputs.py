@@ -238,6 +238,18 @@ def paged_case(seed: int, seq_lens, hq: int, hkv: int, d: int, block_size: int =
     }
 
 
+def paged_fp8_case(seed: int, seq_lens, hq: int, hkv: int, d: int, block_size: int = 16,
+                   pad_blocks: int = 0) -> dict:
+    """``paged_case`` with the K and V pools in FP8 E4M3 (per-tensor descale
+    amax/448 of the same float32 draws); q stays bf16."""
+    c = paged_case(seed, seq_lens, hq, hkv, d, block_size=block_size, pad_blocks=pad_blocks)
+    nb = c["num_blocks"]
+    k8, kd = to_fp8(normal_f32(seed, STREAM_K, (nb, hkv, block_size, d)))
+    v8, vd = to_fp8(normal_f32(seed, STREAM_V, (nb, hkv, block_size, d)))
+    c.update(k_pool=k8, v_pool=v8, descale=(kd, vd), dtype="fp8")
+    return c
+
+
 def paged_prefill_case(seed: int, q_lens, k_lens, hq: int, hkv: int, d: int, block_size: int = 16,
                        pad_blocks: int = 0) -> dict:
     """Chunks of new queries over a shuffled block pool (bf16).

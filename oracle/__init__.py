@@ -276,6 +276,27 @@ def fp8_varlen(q8, k8, v8, cu_seqlens, descale, *, causal: bool, scale: float | 
     return varlen(q, k, v, cu_seqlens, causal=causal, scale=scale, rows=rows, nthreads=nthreads, lib=lib)
 
 
+def _widen(x):
+    """bf16 bit patterns (uint16) -> float64 exactly; floats pass through."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def decode_paged_fp8(q, k8_pool, v8_pool, block_table, seq_lens, descale, *, scale: float | None = None,
+                     rows=None, nthreads: int = 0, lib=None):
+    """Paged decode over FP8 E4M3 pools with per-tensor descale factors
+    (k, v): ``decode_paged`` on q (bf16 widened exactly) and the pools
+    descale * value(code), with the layouts and return values of
+    ``decode_paged``."""
+    kd, vd = (float(x) for x in descale)
+    kp = decode_e4m3(k8_pool, lib=lib) * kd
+    vp = decode_e4m3(v8_pool, lib=lib) * vd
+    return decode_paged(_widen(q), kp, vp, block_table, seq_lens, scale=scale, rows=rows, nthreads=nthreads,
+                        lib=lib)
+
+
 def dropout_threshold(p: float) -> int:
     """Byte threshold t of a dropout probability: t = rint(256 p), p in [0, 1)
     with t <= 255; a weight is kept iff its random byte >= t, with probability

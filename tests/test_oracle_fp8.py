@@ -78,6 +78,23 @@ def test_fp8_varlen_equals_fp8_dense_per_sequence():
             np.testing.assert_array_equal(lse[:, a:b], ld[0])
 
 
+def test_decode_paged_fp8_equals_decode_on_hand_decoded_pools():
+    c = inputs.paged_fp8_case(73, [5, 0, 40, 17], 4, 2, 16)
+    kd, vd = (float(x) for x in c["descale"])
+    o, lse = oracle.decode_paged_fp8(c["q"], c["k_pool"], c["v_pool"], c["block_table"], c["seq_lens"], (kd, vd))
+    q = torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).double().numpy()
+    kp = torch.from_numpy(c["k_pool"]).view(torch.float8_e4m3fn).double().numpy() * kd
+    vp = torch.from_numpy(c["v_pool"]).view(torch.float8_e4m3fn).double().numpy() * vd
+    o2, l2 = oracle.decode_paged(q, kp, vp, c["block_table"], c["seq_lens"])
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, l2)
+    # V's descale scales O only; K's acts through the scores
+    o3, l3 = oracle.decode_paged_fp8(c["q"], c["k_pool"], c["v_pool"], c["block_table"], c["seq_lens"],
+                                     (kd, 2 * vd))
+    np.testing.assert_allclose(o3, 2 * o, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(l3, lse)
+
+
 def test_v_descale_scales_output_only():
     q8, k8, v8, (qd, kd, vd) = _case(72)
     o1, l1 = oracle.fp8_dense(q8, k8, v8, (qd, kd, vd), causal=True)
