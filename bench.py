@@ -11,7 +11,8 @@ workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
 same way and reported in "decode"; the long-context, varlen, chunked paged
 prefill, FP8 prefill, dropout prefill and head_dim 256 prefill workloads are
 reported in "extra" (FP8 against the 5.0 PFLOP/s dense fp8 peak), as is a
-head_dim 256 paged decode workload (GB/s).
+head_dim 256 paged decode workload and the paged decode workload over an FP8
+KV cache (GB/s).
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -43,6 +44,7 @@ KERNEL_SOURCES = {
     "d256": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16_d256.hip"],
     "varlen": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "decode_d256": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
+    "decode_fp8": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
 }
 
 
@@ -57,7 +59,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "dropout",
-                                                 "d256", "decode_d256", "copy"],
+                                                 "d256", "decode_d256", "decode_fp8", "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -273,25 +275,35 @@ def run_fp8(fa, case, steps, warmup, torch, np):
 
 
 def run_decode(fa, case, steps, warmup, torch, np, flush=None, kind="decode"):
+    kv8 = case["dtype"] == "fp8"
     q = bf16_dev(case["q"], torch, np)
-    kp = bf16_dev(case["k_pool"], torch, np)
-    vp = bf16_dev(case["v_pool"], torch, np)
+    kp = torch.from_numpy(case["k_pool"]).cuda() if kv8 else bf16_dev(case["k_pool"], torch, np)
+    vp = torch.from_numpy(case["v_pool"]).cuda() if kv8 else bf16_dev(case["v_pool"], torch, np)
     bt = torch.from_numpy(case["block_table"]).cuda()
     sl = torch.from_numpy(case["seq_lens"]).cuda()
     maxlen = int(case["seq_lens"].max())
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
-    ws = torch.empty(fa.fa_decode_paged_workspace_size(q, kp, vp, bt, sl, maxlen), dtype=torch.uint8,
-                     device="cuda")
-    splits = fa.fa_decode_paged_num_splits(q, kp, vp, bt, sl, maxlen)
+    if kv8:
+        ws = torch.empty(fa.fa_decode_paged_fp8_workspace_size(q, kp, vp, bt, sl, maxlen, case["descale"]),
+                         dtype=torch.uint8, device="cuda")
+        splits = fa.fa_decode_paged_fp8_num_splits(q, kp, vp, bt, sl, maxlen, case["descale"])
+    else:
+        ws = torch.empty(fa.fa_decode_paged_workspace_size(q, kp, vp, bt, sl, maxlen), dtype=torch.uint8,
+                         device="cuda")
+        splits = fa.fa_decode_paged_num_splits(q, kp, vp, bt, sl, maxlen)
 
-    def step():
-        fa.fa_decode_paged(q, kp, vp, bt, sl, maxlen, out=o, lse=lse, workspace=ws)
+    if kv8:
+        def step():
+            fa.fa_decode_paged_fp8(q, kp, vp, bt, sl, maxlen, case["descale"], out=o, lse=lse, workspace=ws)
+    else:
+        def step():
+            fa.fa_decode_paged(q, kp, vp, bt, sl, maxlen, out=o, lse=lse, workspace=ws)
 
     ms, wall_ms = time_steps(step, steps, warmup, torch)
     L = case["seq_lens"].astype(np.int64)
     hkv, d, bs = case["hkv"], case["d"], case["block_size"]
-    kv_bytes = float(2 * hkv * d * 2 * L.sum())
+    kv_bytes = float(2 * hkv * d * (1 if kv8 else 2) * L.sum())
     other = float(q.numel() * 2 + o.numel() * 2 + 4 * ((L + bs - 1) // bs).sum() + 4 * L.size)
     nbytes = kv_bytes + other
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -371,6 +383,9 @@ def main():
     if want("decode_d256", not args.no_extra):
         case = inputs.workload(10)
         out["decode_d256"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, kind="decode_d256"))
+    if want("decode_fp8", not args.no_extra):
+        case = inputs.workload(11)
+        out["decode_fp8"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, kind="decode_fp8"))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, flush))
@@ -413,7 +428,7 @@ def main():
         flush = None
         line["decode"]["copy_gbs"] = round(copy_bandwidth(torch), 1)
     extra = []
-    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256", "decode_d256"):
+    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256", "decode_d256", "decode_fp8"):
         if key in out:
             c, r = out[key]
             if "gbs" in r:

@@ -81,9 +81,9 @@ fa_status check_decode(const fa_decode_paged_args* a) {
 }
 
 // Parts the key-block list is cut into; -1 if the device cannot be queried.
-int decode_parts(const fa_decode_paged_args* a) {
+int decode_parts(const fa_decode_paged_args* a, bool kv8) {
   return fa::decode_num_parts(a->num_splits, a->batch, a->heads_q, a->heads_q / a->heads_kv, a->max_seq_len,
-                              a->head_dim);
+                              a->head_dim, kv8);
 }
 
 
@@ -417,9 +417,10 @@ FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
   return ok();
 }
 
-FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) {
+namespace {
+size_t decode_workspace(const fa_decode_paged_args* a, bool kv8) {
   if (check_decode(a) != FA_OK) return 0;
-  const int parts = decode_parts(a);
+  const int parts = decode_parts(a, kv8);
   if (parts < 1) {
     fail(FA_ERR_HIP, "fa_decode_paged_workspace_size: cannot query the current device");
     return 0;
@@ -427,37 +428,55 @@ FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) {
   return fa::decode_workspace_bytes(parts, a->batch, a->heads_q, a->head_dim);
 }
 
-FA_EXPORT int32_t fa_decode_paged_num_splits(const fa_decode_paged_args* a) {
+int32_t decode_splits(const fa_decode_paged_args* a, bool kv8) {
   if (check_decode(a) != FA_OK) return 0;
-  const int parts = decode_parts(a);
+  const int parts = decode_parts(a, kv8);
   if (parts < 1) {
     fail(FA_ERR_HIP, "fa_decode_paged_num_splits: cannot query the current device");
     return 0;
   }
   return parts;
 }
+}  // namespace
 
-FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream) {
+FA_EXPORT size_t fa_decode_paged_workspace_size(const fa_decode_paged_args* a) { return decode_workspace(a, false); }
+
+FA_EXPORT int32_t fa_decode_paged_num_splits(const fa_decode_paged_args* a) { return decode_splits(a, false); }
+
+FA_EXPORT size_t fa_decode_paged_fp8_workspace_size(const fa_decode_paged_fp8_args* a) {
+  return a ? decode_workspace(&a->base, true) : 0;
+}
+
+FA_EXPORT int32_t fa_decode_paged_fp8_num_splits(const fa_decode_paged_fp8_args* a) {
+  return a ? decode_splits(&a->base, true) : 0;
+}
+
+namespace {
+// Paged decode over bf16 pools, or E4M3 pools (kv8) with descale factors.
+fa_status decode_impl(const fa_decode_paged_args* a, bool kv8, float k_descale, float v_descale, const char* fn,
+                      void* stream) {
   const fa_status st = check_decode(a);
   if (st != FA_OK) return st;
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
-    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: scale must be positive and finite");
+    return fail(FA_ERR_BAD_SHAPE, "%s: scale must be positive and finite", fn);
+  if (kv8 && (!(k_descale > 0.f) || !std::isfinite(k_descale) || !(v_descale > 0.f) || !std::isfinite(v_descale)))
+    return fail(FA_ERR_BAD_SHAPE, "%s: descale factors must be positive and finite", fn);
   if (a->batch == 0) return ok();
   if (!a->q || !a->seq_lens || !a->o || !a->workspace)
-    return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: q, seq_lens, o and workspace are required");
+    return fail(FA_ERR_NULL_POINTER, "%s: q, seq_lens, o and workspace are required", fn);
   if (a->max_seq_len > 0 && (!a->k_pool || !a->v_pool || !a->block_table))
-    return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: pools and block_table are required when max_seq_len > 0");
-  if (!strides_ok(a->pool_stride, 3, 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
-    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: strides must be non-negative multiples of 8 elements");
+    return fail(FA_ERR_NULL_POINTER, "%s: pools and block_table are required when max_seq_len > 0", fn);
+  // 16-byte loads: pool strides are multiples of 16 bytes (8 bf16 elements, 16 E4M3 bytes)
+  if (!strides_ok(a->pool_stride, 3, kv8 ? 16 : 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
+    return fail(FA_ERR_BAD_SHAPE, "%s: strides must be non-negative multiples of 16 bytes", fn);
   if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->o) ||
       !aligned16(a->workspace))
-    return fail(FA_ERR_BAD_SHAPE, "fa_decode_paged: q, pools, o and workspace must be 16-byte aligned");
-  const int parts = decode_parts(a);
-  if (parts < 1) return fail(FA_ERR_HIP, "fa_decode_paged: cannot query the current device");
+    return fail(FA_ERR_BAD_SHAPE, "%s: q, pools, o and workspace must be 16-byte aligned", fn);
+  const int parts = decode_parts(a, kv8);
+  if (parts < 1) return fail(FA_ERR_HIP, "%s: cannot query the current device", fn);
   const size_t need = fa::decode_workspace_bytes(parts, a->batch, a->heads_q, a->head_dim);
   if (a->workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "fa_decode_paged: workspace %zu bytes, need %zu", a->workspace_bytes,
-                need);
+    return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn, a->workspace_bytes, need);
 
   fa::DecodeParams p{};
   p.q = a->q;
@@ -480,10 +499,22 @@ FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream)
   p.group = a->heads_q / a->heads_kv;
   p.max_blocks = a->max_blocks_per_seq;
   p.max_seq_len = a->max_seq_len;
-  p.scale_log2 = scale_log2(a->scale);
+  p.scale_log2 = kv8 ? (float)((double)a->scale * k_descale * 1.4426950408889634073599) : scale_log2(a->scale);
+  p.kv8 = kv8 ? 1 : 0;
+  p.o_scale = kv8 ? v_descale : 1.f;
   const hipError_t e = fa::launch_decode_paged(p, a->head_dim, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode_paged: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream) {
+  return decode_impl(a, false, 1.f, 1.f, "fa_decode_paged", stream);
+}
+
+FA_EXPORT fa_status fa_decode_paged_fp8(const fa_decode_paged_fp8_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_decode_paged_fp8: args is NULL");
+  return decode_impl(&a->base, true, a->k_descale, a->v_descale, "fa_decode_paged_fp8", stream);
 }
 
 FA_EXPORT const char* fa_status_string(fa_status status) {

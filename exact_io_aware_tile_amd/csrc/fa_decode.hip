@@ -47,6 +47,13 @@
 // Lazy correction: weights are formed against the head's current reference
 // max until one would exceed 2^8; only then is the reference moved (the max
 // over the four lane groups holding that head) and (o, l) rescaled.
+// FP8 pools (KV8): K and V blocks are E4M3 bytes, widened to bf16 in
+// registers right after the load (exact: every E4M3 value is a bf16 value),
+// so the products and the LDS copy are the bf16 ones; the K descale factor
+// is folded into the score scale and the V descale into the combine.  A
+// 16-byte K load then covers two score steps: the contraction is relabelled
+// so that step 2u + h takes head dims 64u + 16(l/16) + 8h .. +7 (Q is loaded
+// with the same relabelling).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -162,32 +169,46 @@ __device__ __forceinline__ int swz(int r, int c) {
 // One block as this lane loads it: k[s] = token l%16, dims 32s + 8(l/16)
 // .. +7 (score A operand); v[s] = token s * 64/(D/8) + l / (D/8), dims
 // 8(l % (D/8)) .. +7 (D/32 loads each).
-template <int D>
+template <int D, bool KV8>
 struct Blk {
-  uint4 k[D / 32];
-  uint4 v[D / 32];
+  uint4 k[KV8 ? D / 64 : D / 32];
+  uint4 v[KV8 ? D / 64 : D / 32];
 };
 
-// Blocks in flight per wave (the register ring): four at head_dim 64 and
-// 128, two at 256, where a block is 16 KB per operand and the ring would
+// Blocks in flight per wave (the register ring): four, or two at head_dim
+// 256 with bf16 pools, where a block is 16 KB per operand and the ring would
 // otherwise take every register.
-template <int D>
-constexpr int ring_depth() { return D == 256 ? 2 : 4; }
+template <int D, bool KV8>
+constexpr int ring_depth() { return D == 256 && !KV8 ? 2 : 4; }
+
+// Two E4M3 bytes (0, 1 or, with HI, 2, 3 of w) -> two bf16, exactly (scale 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Eight E4M3 bytes (two words) -> eight bf16.
+__device__ __forceinline__ uint4 e4m3x8_bf16x8(uint32_t a, uint32_t b) {
+  return make_uint4(e4m3x2_bf16x2<false>(a), e4m3x2_bf16x2<true>(a), e4m3x2_bf16x2<false>(b),
+                    e4m3x2_bf16x2<true>(b));
+}
 
 // Waves per SIMD the split kernel is built for: two, or one at head_dim 256
 // (its ring, accumulator and Q fragments need more than 256 registers; the
 // rest goes to the accumulation registers).
-template <int D>
-constexpr int split_waves_per_simd() { return D == 256 ? 1 : 2; }
+template <int D, bool KV8 = false>
+constexpr int split_waves_per_simd() { return D == 256 ? 1 : (KV8 ? 3 : 2); }
 
-template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<D>(),
-                                                                     split_waves_per_simd<D>()))) void
+template <int D, bool KV8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<D, KV8>(),
+                                                                     split_waves_per_simd<D, KV8>()))) void
 decode_split_kernel(const DecodeParams p) {
   constexpr int kD = D;
-  constexpr int NS = D / 32;       // 32-dim steps of the score product; value loads per lane
-  constexpr int VCH = D / 8;       // 16-byte chunks of a value row
-  constexpr int VTPL = 64 / VCH;   // value rows per load instruction
+  constexpr int ES = KV8 ? 1 : 2;       // bytes per pool element
+  constexpr int NS = D / 32;            // 32-dim steps of the score product
+  constexpr int NL = KV8 ? D / 64 : NS; // 16-byte loads per lane per operand and block
+  constexpr int VCH = D / 8;            // 16-byte bf16 chunks of a value row in LDS
+  constexpr int VCHL = D * ES / 16;     // 16-byte pieces of a value row in the pool
+  constexpr int VTPL = 64 / VCHL;       // value rows per load instruction
   const int part = blockIdx.x;
   const int g = blockIdx.y;  // kv head; query heads g*G .. g*G + G - 1
   const int G = p.group;
@@ -214,22 +235,25 @@ decode_split_kernel(const DecodeParams p) {
   // Loads address a block through a wave-uniform 64-bit base (scalar
   // registers) plus a per-lane 32-bit byte offset that is the same for every
   // block (the host keeps it below 2^31).
-  const char* __restrict__ kpool = (const char*)p.k_pool + (int64_t)g * p.p_hs * 2;
-  const char* __restrict__ vpool = (const char*)p.v_pool + (int64_t)g * p.p_hs * 2;
-  uint32_t koff[NS], voff[NS];
+  const char* __restrict__ kpool = (const char*)p.k_pool + (int64_t)g * p.p_hs * ES;
+  const char* __restrict__ vpool = (const char*)p.v_pool + (int64_t)g * p.p_hs * ES;
+  uint32_t koff[NL], voff[NL];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    koff[s] = (uint32_t)((n * p.p_ts + 32 * s + 8 * j) * 2);
-    voff[s] = (uint32_t)(((s * VTPL + lane / VCH) * p.p_ts + 8 * (lane % VCH)) * 2);
+  for (int s = 0; s < NL; ++s) {
+    koff[s] = KV8 ? (uint32_t)(n * p.p_ts + 64 * s + 16 * j) : (uint32_t)((n * p.p_ts + 32 * s + 8 * j) * 2);
+    voff[s] = (uint32_t)((s * VTPL + lane / VCHL) * p.p_ts * ES + 16 * (lane % VCHL));
   }
 
   // Q of head n as the B operand of the score product (zero for columns
   // past the group).
   uint4 qf[NS];
   auto load_q = [&](int b) {
-    const uint16_t* qr = (const uint16_t*)p.q + (int64_t)b * p.q_bs + (int64_t)(g * G + n) * p.q_hs + 8 * j;
+    const uint16_t* qr = (const uint16_t*)p.q + (int64_t)b * p.q_bs + (int64_t)(g * G + n) * p.q_hs;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = n < G ? *(const uint4*)(qr + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
+    for (int s = 0; s < NS; ++s) {
+      const int dim = KV8 ? 64 * (s >> 1) + 16 * j + 8 * (s & 1) : 32 * s + 8 * j;
+      qf[s] = n < G ? *(const uint4*)(qr + dim) : make_uint4(0u, 0u, 0u, 0u);
+    }
   };
   load_q(pc.b);
 
@@ -245,15 +269,15 @@ decode_split_kernel(const DecodeParams p) {
   reset();
 
   int n_issued = 0;
-  auto issue = [&](Blk<D>& B) {
+  auto issue = [&](Blk<D, KV8>& B) {
     if (n_issued < n_units) {
-      const int64_t base = (int64_t)p.block_table[(int64_t)ic.b * p.max_blocks + ic.blk] * p.p_bs * 2;
+      const int64_t base = (int64_t)p.block_table[(int64_t)ic.b * p.max_blocks + ic.blk] * p.p_bs * ES;
       const char* kb = kpool + base;
       const char* vb = vpool + base;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) B.k[s] = load_stream(kb + koff[s]);
+      for (int s = 0; s < NL; ++s) B.k[s] = load_stream(kb + koff[s]);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) B.v[s] = load_stream(vb + voff[s]);
+      for (int s = 0; s < NL; ++s) B.v[s] = load_stream(vb + voff[s]);
       if (++n_issued < n_units) cursor_next(p, ic);
     }
   };
@@ -264,19 +288,31 @@ decode_split_kernel(const DecodeParams p) {
 
   // One block through the recurrence; tokens at or past VALID hold no key
   // (only a sequence's last block has such tokens).
-  auto process = [&](const Blk<D>& B, int valid) {
-    // Values to LDS (row = token, swizzled chunks).
+  auto process = [&](const Blk<D, KV8>& B, int valid) {
+    // Values to LDS (row = token, swizzled bf16 chunks).
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int r = s * VTPL + lane / VCH;
-      *(uint4*)&v_s[r * kD + swz<D>(r, lane % VCH) * 8] = B.v[s];
+    for (int s = 0; s < NL; ++s) {
+      const int r = s * VTPL + lane / VCHL;
+      if (KV8) {
+        const int c = 2 * (lane % VCHL);  // 16 E4M3 bytes = bf16 chunks c, c + 1
+        *(uint4*)&v_s[r * kD + swz<D>(r, c) * 8] = e4m3x8_bf16x8(B.v[s].x, B.v[s].y);
+        *(uint4*)&v_s[r * kD + swz<D>(r, c + 1) * 8] = e4m3x8_bf16x8(B.v[s].z, B.v[s].w);
+      } else {
+        *(uint4*)&v_s[r * kD + swz<D>(r, lane % VCH) * 8] = B.v[s];
+      }
     }
     // Scores: sc[r] = S[token 4j + r][head n].
     f32x4 sc = zero4();
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, B.k[s]),
-                                                  __builtin_bit_cast(bf16x8, qf[s]), sc, 0, 0, 0);
+    for (int s = 0; s < NS; ++s) {
+      uint4 ka;
+      if (KV8)
+        ka = (s & 1) ? e4m3x8_bf16x8(B.k[s >> 1].z, B.k[s >> 1].w) : e4m3x8_bf16x8(B.k[s >> 1].x, B.k[s >> 1].y);
+      else
+        ka = B.k[s];
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qf[s]),
+                                                  sc, 0, 0, 0);
+    }
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = 4 * j + r < valid ? sc[r] * cs : -INFINITY;
@@ -343,7 +379,7 @@ decode_split_kernel(const DecodeParams p) {
   };
 
   int n_done = 0;
-  auto step = [&](const Blk<D>& B) {
+  auto step = [&](const Blk<D, KV8>& B) {
     if (n_done >= n_units) return;
     const bool last_blk = pc.blk == pc.nb - 1;
     process(B, last_blk ? pc.L - pc.blk * kBlock : kBlock);
@@ -363,15 +399,15 @@ decode_split_kernel(const DecodeParams p) {
   // The scheduling barriers keep each ring refill where it is written, three
   // blocks ahead of its use, instead of letting the scheduler sink the loads
   // next to their consumers.
-  Blk<D> R0, R1, R2, R3;
+  Blk<D, KV8> R0, R1, R2, R3;
   issue(R0);
   issue(R1);
-  if constexpr (ring_depth<D>() == 4) {
+  if constexpr (ring_depth<D, KV8>() == 4) {
     issue(R2);
     issue(R3);
   }
   __builtin_amdgcn_sched_barrier(0);
-  for (int u = 0; u < n_units; u += ring_depth<D>()) {
+  for (int u = 0; u < n_units; u += ring_depth<D, KV8>()) {
     step(R0);
     __builtin_amdgcn_sched_barrier(0);
     issue(R0);
@@ -380,7 +416,7 @@ decode_split_kernel(const DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     issue(R1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ring_depth<D>() == 4) {
+    if constexpr (ring_depth<D, KV8>() == 4) {
       step(R2);
       __builtin_amdgcn_sched_barrier(0);
       issue(R2);
@@ -439,8 +475,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
     }
   }
   // o / lb: the weights P.V used, so the row is a convex combination of
-  // value rows up to fp32 rounding; LSE from the fp32 weights.
-  const float inv = lb > 0.f ? 1.f / lb : 0.f;
+  // value rows up to fp32 rounding (times the V descale of FP8 pools); LSE
+  // from the fp32 weights.
+  const float inv = lb > 0.f ? p.o_scale / lb : 0.f;
   uint16_t* orow = (uint16_t*)p.o + (int64_t)b * p.o_bs + (int64_t)h * p.o_hs;
   if constexpr (DPL == 1) {
     orow[lane] = (uint16_t)(pack_bf16x2(oa[0] * inv, 0.f) & 0xFFFFu);
@@ -454,18 +491,20 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
 
 }  // namespace
 
-int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim) {
+int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim,
+                     bool kv8) {
   if (num_splits > 0) return num_splits;
   // One part per wave slot of the device (the split kernel is built for two
-  // waves per SIMD, eight per CU; one and four at head_dim 256), spread over
-  // the kv heads; no more parts than about one per 4 blocks of the largest
-  // possible batch.
+  // waves per SIMD, eight per CU; one and four at head_dim 256; three and
+  // twelve for FP8 pools below 256), spread over the kv heads; no more parts
+  // than about one per 4 blocks of the largest possible batch.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   const int64_t heads_kv = group > 0 ? heads_q / group : 1;
-  const int waves_per_cu = head_dim == 256 ? 4 * split_waves_per_simd<256>() : kSplitWavesPerCu;
+  const int waves_per_cu =
+      head_dim == 256 ? 4 * split_waves_per_simd<256>() : (kv8 ? 4 * split_waves_per_simd<128, true>() : kSplitWavesPerCu);
   int64_t parts = (int64_t)cus * waves_per_cu / (heads_kv > 0 ? heads_kv : 1);
   const int64_t max_units = (int64_t)batch * ((max_seq_len + kBlock - 1) / kBlock);
   if (parts > (max_units + 3) / 4) parts = (max_units + 3) / 4;
@@ -481,7 +520,10 @@ size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim) {
 namespace {
 template <int D>
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(p.num_splits, p.heads_kv), dim3(64), 0, stream, p);
+  if (p.kv8)
+    hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(p.num_splits, p.heads_kv), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(p.num_splits, p.heads_kv), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(p.heads_q, p.batch), dim3(64), 0, stream, p);

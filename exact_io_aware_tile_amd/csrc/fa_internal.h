@@ -84,7 +84,9 @@ struct DecodeParams {
   float* ws_ml;  // [heads_q, num_splits + batch, 4] fp32 partial (m, l, lb, -), m in base 2
   int32_t batch, heads_q, heads_kv, group, max_blocks, max_seq_len;
   int32_t num_splits;  // parts the block list of one kv head is cut into
-  float scale_log2;
+  float scale_log2;    // FP8 pools: times the K descale factor
+  int32_t kv8;         // pools hold E4M3 bytes (strides then count bytes)
+  float o_scale;       // multiplies O: 1, or the V descale factor of FP8 pools
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
@@ -98,7 +100,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams& p, int head_dim, hipStream_t stream);
 // Parts for a requested num_splits (0: one per wave slot of the current
 // device, or of a 256-CU device when none can be queried).
-int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim);
+int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim, bool kv8);
 size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim);
 
 }  // namespace fa

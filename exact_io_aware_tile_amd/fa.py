@@ -14,6 +14,7 @@ Layouts (see include/fa.h):
                      of the weights drawn from (dropout_p, seed, offset)
     fa_fwd_paged:    q [Tq, Hq, d] (chunks packed by cu_seqlens_q int32 [S+1]), pools and
                      block_table as for decode, seq_lens_k int32 [S] -> o like q, lse [Hq, Tq]
+    fa_decode_paged_fp8: as fa_decode_paged with uint8 E4M3 pools and (k, v) descale factors
     fa_decode_paged: q [B, Hq, d], pools [blocks, Hkv, 16, d] (or any strides with d
                      contiguous), block_table int32 [B, max_blocks], seq_lens int32 [B]
                      -> o [B, Hq, d], lse [B, Hq]
@@ -83,6 +84,10 @@ class DecodePagedArgs(ctypes.Structure):
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class DecodePagedFp8Args(ctypes.Structure):
+    _fields_ = [("base", DecodePagedArgs), ("k_descale", _F), ("v_descale", _F)]
+
+
 class FwdPagedArgs(ctypes.Structure):
     _fields_ = [("q", _P), ("k_pool", _P), ("v_pool", _P), ("pool_stride", _I64 * 3),
                 ("block_table", _P), ("cu_seqlens_q", _P), ("seq_lens_k", _P), ("o", _P), ("lse", _P),
@@ -93,7 +98,8 @@ class FwdPagedArgs(ctypes.Structure):
 
 
 SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_fp8", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
-           "fa_decode_paged_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
+           "fa_decode_paged_num_splits", "fa_decode_paged_fp8", "fa_decode_paged_fp8_workspace_size",
+           "fa_decode_paged_fp8_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -128,6 +134,12 @@ def lib(path: str = LIB_PATH):
     L.fa_fwd_paged.restype = ctypes.c_int
     L.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
     L.fa_decode_paged.restype = ctypes.c_int
+    L.fa_decode_paged_fp8.argtypes = [ctypes.POINTER(DecodePagedFp8Args), _P]
+    L.fa_decode_paged_fp8.restype = ctypes.c_int
+    L.fa_decode_paged_fp8_workspace_size.argtypes = [ctypes.POINTER(DecodePagedFp8Args)]
+    L.fa_decode_paged_fp8_workspace_size.restype = ctypes.c_size_t
+    L.fa_decode_paged_fp8_num_splits.argtypes = [ctypes.POINTER(DecodePagedFp8Args)]
+    L.fa_decode_paged_fp8_num_splits.restype = _I32
     L.fa_decode_paged_workspace_size.argtypes = [ctypes.POINTER(DecodePagedArgs)]
     L.fa_decode_paged_workspace_size.restype = ctypes.c_size_t
     L.fa_decode_paged_num_splits.argtypes = [ctypes.POINTER(DecodePagedArgs)]
@@ -434,3 +446,54 @@ def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, 
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check(lib().fa_decode_paged(ctypes.byref(a), _stream(stream)))
     return out, lse
+
+
+def fa_decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, descale, *,
+                        scale: float | None = None, num_splits: int = 0, out=None, lse=None,
+                        return_lse: bool = True, workspace=None, stream=None):
+    """Paged single-token decode over an FP8 KV cache: uint8 E4M3 pools
+    standing for descale[0] * value(k code) and descale[1] * value(v code);
+    q and o bf16.  Returns (o, lse)."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse)
+    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise TypeError("fa_decode_paged_fp8 takes E4M3 pools as uint8 tensors")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    a = DecodePagedFp8Args()
+    a.base = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, num_splits)
+    a.base.o, a.base.lse = _ptr(out), _ptr(lse)
+    a.base.o_stride[:] = list(out.stride()[:2])
+    a.k_descale, a.v_descale = (float(x) for x in descale)
+    need = int(lib().fa_decode_paged_fp8_workspace_size(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a.base.workspace, a.base.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check(lib().fa_decode_paged_fp8(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def _decode_fp8_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, descale, num_splits):
+    a = DecodePagedFp8Args()
+    a.base = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, None, num_splits)
+    a.k_descale, a.v_descale = (float(x) for x in descale)
+    return a
+
+
+def fa_decode_paged_fp8_workspace_size(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, descale, *,
+                                       num_splits: int = 0) -> int:
+    a = _decode_fp8_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, descale, num_splits)
+    return int(lib().fa_decode_paged_fp8_workspace_size(ctypes.byref(a)))
+
+
+def fa_decode_paged_fp8_num_splits(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, descale, *,
+                                   num_splits: int = 0) -> int:
+    a = _decode_fp8_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, descale, num_splits)
+    return int(lib().fa_decode_paged_fp8_num_splits(ctypes.byref(a)))

@@ -292,7 +292,8 @@ def workload(n: int) -> dict:
     (the usual training rate), seed 8, offset 0; 9. bf16 causal GQA prefill
     at head_dim 256, batch 2, 16 q heads / 8 kv heads, N = 4096 (the shape of
     a head_dim-256 model's prefill); 10. bf16 paged GQA decode at head_dim
-    256, batch 32, 16 q heads / 8 kv heads, lengths U{1024..16384}.
+    256, batch 32, 16 q heads / 8 kv heads, lengths U{1024..16384}; 11.
+    workload 5 with an FP8 E4M3 KV cache (per-tensor descale amax/448).
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -315,6 +316,11 @@ def workload(n: int) -> dict:
         lens = varlen_lengths(5, 64, 1024, 32768)
         c = paged_case(5, lens, 32, 8, 128, block_size=16)
         c.update(name="bf16 paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
+        return c
+    if n == 11:
+        lens = varlen_lengths(5, 64, 1024, 32768)
+        c = paged_fp8_case(5, lens, 32, 8, 128, block_size=16)
+        c.update(name="fp8 kv paged GQA decode B=64 Hq=32 Hkv=8 d=128 L~U{1024..32768} block 16")
         return c
     if n == 10:
         lens = varlen_lengths(10, 32, 1024, 16384)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_OK = 0,
@@ -348,6 +348,28 @@ fa_status fa_decode_paged(const fa_decode_paged_args *args, void *stream);
 /* The number of parts fa_decode_paged will cut each KV head's key blocks
  * into for these arguments (0 on invalid arguments). */
 int32_t fa_decode_paged_num_splits(const fa_decode_paged_args *args);
+
+/*
+ * fa_decode_paged_fp8 -- fa_decode_paged over an FP8 KV cache: k_pool and
+ * v_pool hold E4M3 codes (one byte each; the OCP format of fa_fwd_fp8)
+ * standing for k_descale * value(code) and v_descale * value(code); q and o
+ * stay bf16.  `base` is read as for fa_decode_paged, with pool_stride in
+ * bytes (multiples of 16, token stride at most 2^26); the workspace size and
+ * split count are reported by fa_decode_paged_fp8_workspace_size() and
+ * fa_decode_paged_fp8_num_splits() (the automatic split count follows this
+ * kernel's occupancy, three waves per SIMD below head_dim 256).  The codes are widened to
+ * bf16 exactly in registers and the products and softmax are those of
+ * fa_decode_paged; K's descale scales the scores and V's the output.
+ * Descale factors must be positive and finite.
+ */
+typedef struct {
+  fa_decode_paged_args base;
+  float k_descale, v_descale;
+} fa_decode_paged_fp8_args;
+
+fa_status fa_decode_paged_fp8(const fa_decode_paged_fp8_args *args, void *stream);
+size_t fa_decode_paged_fp8_workspace_size(const fa_decode_paged_fp8_args *args);
+int32_t fa_decode_paged_fp8_num_splits(const fa_decode_paged_fp8_args *args);
 
 /* Static text for a status code. */
 const char *fa_status_string(fa_status status);

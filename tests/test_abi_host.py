@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 6
+    assert L.fa_abi_version() == declared == 7
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -70,6 +70,7 @@ STRUCTS = {
     "fa_decode_paged_args": fa.DecodePagedArgs,
     "fa_dropout_args": fa.DropoutArgs,
     "fa_fwd_varlen_fp8_args": fa.FwdVarlenFp8Args,
+    "fa_decode_paged_fp8_args": fa.DecodePagedFp8Args,
 }
 
 
@@ -381,6 +382,42 @@ def test_decode_rejects_before_launch(L, kw, status):
     a = decode_args(**kw)
     assert L.fa_decode_paged(ctypes.byref(a), None) == status
     assert L.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,dkw,status", [
+    (dict(), dict(k_descale=0.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(), dict(v_descale=float("inf")), fa.FA_ERR_BAD_SHAPE),
+    (dict(pool_stride=[8 * 16 * 128, 16 * 128, 120]), {}, fa.FA_ERR_BAD_SHAPE),   # 120-byte token stride
+    (dict(head_dim=96), {}, fa.FA_ERR_UNSUPPORTED),
+    (dict(heads_q=30), {}, fa.FA_ERR_BAD_SHAPE),
+    (dict(workspace=None), {}, fa.FA_ERR_NULL_POINTER),
+    (dict(), {}, fa.FA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_fp8_rejects_before_launch(L, kw, dkw, status):
+    a = fa.DecodePagedFp8Args()
+    a.base = decode_args(**kw)
+    a.k_descale, a.v_descale = 0.01, 0.02
+    for k, v in dkw.items():
+        setattr(a, k, v)
+    assert L.fa_decode_paged_fp8(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+    assert L.fa_decode_paged_fp8(None, None) == fa.FA_ERR_NULL_POINTER
+
+
+def test_decode_fp8_sizes(L):
+    a = fa.DecodePagedFp8Args()
+    a.base = decode_args(num_splits=6)
+    a.k_descale, a.v_descale = 0.01, 0.02
+    assert L.fa_decode_paged_fp8_num_splits(ctypes.byref(a)) == 6
+    assert L.fa_decode_paged_fp8_workspace_size(ctypes.byref(a)) == 32 * (6 + 4) * (128 + 4) * 4
+    # automatic: twelve wave slots per CU (three per SIMD) for FP8 pools,
+    # still capped at about one part per 4 blocks of the largest batch
+    a.base = decode_args(max_seq_len=64 * 16, max_blocks_per_seq=64, batch=64)
+    ns8 = L.fa_decode_paged_fp8_num_splits(ctypes.byref(a))
+    ns16 = L.fa_decode_paged_num_splits(ctypes.byref(a.base))
+    assert ns8 >= ns16 and 1 <= ns8 <= 64 * 64 // 4
+    assert L.fa_decode_paged_fp8_num_splits(None) == 0
+    assert L.fa_decode_paged_fp8_workspace_size(None) == 0
 
 
 def test_decode_workspace_scales_with_head_dim(L):

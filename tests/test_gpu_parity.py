@@ -478,6 +478,68 @@ def test_decode_head_dims_paged_equals_contiguous_bitwise(gpu, d):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def decode_fp8_gpu(fa, case, num_splits=0, k_pool=None, v_pool=None, table=None):
+    q = dev(case["q"], "bf16")
+    kp = torch.from_numpy(case["k_pool"]).cuda() if k_pool is None else k_pool
+    vp = torch.from_numpy(case["v_pool"]).cuda() if v_pool is None else v_pool
+    bt = torch.from_numpy(case["block_table"]).cuda() if table is None else table
+    sl = torch.from_numpy(case["seq_lens"]).cuda()
+    maxlen = int(case["seq_lens"].max(initial=0))
+    o, lse = fa.fa_decode_paged_fp8(q, kp, vp, bt, sl, maxlen, case["descale"], num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("group", [1, 4, 16])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_decode_fp8_kv_parity(gpu, d, group, num_splits):
+    """FP8 KV cache: the codes are widened exactly, so the bf16 decode
+    tolerance applies to the attention of q over descale * value(code)."""
+    lens = [1, 16, 17, 100, 0, 333, 48, 1000]
+    hkv = 2
+    case = inputs.paged_fp8_case(360 + group + d, lens, hkv * group, hkv, d, pad_blocks=2)
+    o, lse = decode_fp8_gpu(gpu, case, num_splits=num_splits)
+    o_ref, lse_ref = oracle.decode_paged_fp8(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                             case["seq_lens"], case["descale"])
+    check(host(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+          f"fp8 kv decode d={d} group={group} splits={num_splits}")
+
+
+def test_decode_fp8_kv_paged_equals_contiguous_bitwise(gpu):
+    lens = [5000, 17, 1024, 333]
+    case = inputs.paged_fp8_case(370, lens, 32, 8, 128)
+    o1, l1 = decode_fp8_gpu(gpu, case)
+    bt = case["block_table"]
+    order = np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(lens)]).astype(np.int64)
+    idx = torch.from_numpy(order).cuda()
+    kp = torch.from_numpy(case["k_pool"]).cuda()[idx].contiguous()
+    vp = torch.from_numpy(case["v_pool"]).cuda()[idx].contiguous()
+    table = np.full_like(bt, -1)
+    pos = 0
+    for b, L in enumerate(lens):
+        nb = (L + 15) // 16
+        table[b, :nb] = np.arange(pos, pos + nb)
+        pos += nb
+    o2, l2 = decode_fp8_gpu(gpu, case, k_pool=kp, v_pool=vp, table=torch.from_numpy(table).cuda())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_fp8_kv_matches_bf16_decode_of_widened_pools(gpu):
+    """The FP8 instance equals the bf16 kernel run on the widened pools with
+    the descales folded into the pool values (both sides exact in bf16 when
+    the descale is a power of two)."""
+    lens = [300, 17, 64]
+    case = inputs.paged_fp8_case(371, lens, 8, 2, 128)
+    case["descale"] = (0.25, 0.5)
+    o8, l8 = decode_fp8_gpu(gpu, case)
+    kw = torch.from_numpy(case["k_pool"]).cuda().view(torch.float8_e4m3fn).float() * 0.25
+    vw = torch.from_numpy(case["v_pool"]).cuda().view(torch.float8_e4m3fn).float() * 0.5
+    o16, l16 = decode_gpu(gpu, case, k_pool=kw.to(torch.bfloat16), v_pool=vw.to(torch.bfloat16))
+    assert (o8.float() - o16.float()).abs().max().item() <= 2e-2
+    assert (l8 - l16).abs().max().item() <= 1e-5
+
+
 @pytest.mark.parametrize("lens", [[0, 0, 5], [5, 0, 0], [0], [16, 0, 16, 0, 1]])
 def test_decode_empty_sequences(gpu, lens):
     case = inputs.paged_case(330 + len(lens), lens, 8, 2, 128, pad_blocks=1)
