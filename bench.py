@@ -332,7 +332,7 @@ def run_copy(torch, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 "
                                    f"(got {args.gpus}). Multi-GPU sharding is described, not built."}))
         sys.exit(2)
     import numpy as np
