@@ -270,6 +270,19 @@ def paged_prefill_case(seed: int, q_lens, k_lens, hq: int, hkv: int, d: int, blo
     return c
 
 
+def paged_prefill_fp8_case(seed: int, q_lens, k_lens, hq: int, hkv: int, d: int, block_size: int = 16,
+                           pad_blocks: int = 0) -> dict:
+    """``paged_prefill_case`` in FP8 E4M3: the same float32 draws of the
+    queries and pools, each tensor with its per-tensor descale amax/448."""
+    c = paged_prefill_case(seed, q_lens, k_lens, hq, hkv, d, block_size=block_size, pad_blocks=pad_blocks)
+    nb = c["num_blocks"]
+    q8, qd = to_fp8(normal_f32(seed, STREAM_QCHUNK, (c["total_q"], hq, d)))
+    k8, kd = to_fp8(normal_f32(seed, STREAM_K, (nb, hkv, block_size, d)))
+    v8, vd = to_fp8(normal_f32(seed, STREAM_V, (nb, hkv, block_size, d)))
+    c.update(q=q8, k_pool=k8, v_pool=v8, descale=(qd, kd, vd), dtype="fp8")
+    return c
+
+
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------

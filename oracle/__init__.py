@@ -297,6 +297,18 @@ def decode_paged_fp8(q, k8_pool, v8_pool, block_table, seq_lens, descale, *, sca
                         lib=lib)
 
 
+def paged_prefill_fp8(q8, k8_pool, v8_pool, block_table, cu_seqlens_q, seq_lens_k, descale, *, causal: bool,
+                      scale: float | None = None, rows=None, nthreads: int = 0, lib=None):
+    """Chunked prefill with FP8 E4M3 queries and pools and per-tensor descale
+    factors (q, k, v): ``paged_prefill`` on descale[i] * value(code)."""
+    qd, kd, vd = (float(x) for x in descale)
+    q = decode_e4m3(q8, lib=lib) * qd
+    kp = decode_e4m3(k8_pool, lib=lib) * kd
+    vp = decode_e4m3(v8_pool, lib=lib) * vd
+    return paged_prefill(q, kp, vp, block_table, cu_seqlens_q, seq_lens_k, causal=causal, scale=scale, rows=rows,
+                         nthreads=nthreads, lib=lib)
+
+
 def dropout_threshold(p: float) -> int:
     """Byte threshold t of a dropout probability: t = rint(256 p), p in [0, 1)
     with t <= 255; a weight is kept iff its random byte >= t, with probability

@@ -312,6 +312,32 @@ def test_decode_max_token_stride(gpu, d):
     torch.cuda.empty_cache()
 
 
+def test_concurrent_streams_bitwise(gpu):
+    """Calls are re-entrant on distinct streams: a prefill and a decode
+    enqueued on two (default-priority) streams at once give the bits each
+    gives alone."""
+    c = inputs.dense_case(90, 2, 700, 700, 4, 2, 128, dtype="bf16")
+    q, k, v = (dev(c[n], "bf16") for n in ("q", "k", "v"))
+    p = inputs.paged_case(91, [3000, 17, 900], 8, 2, 128)
+    dq, kp, vp = dev(p["q"], "bf16"), dev(p["k_pool"], "bf16"), dev(p["v_pool"], "bf16")
+    bt, sl = torch.from_numpy(p["block_table"]).cuda(), torch.from_numpy(p["seq_lens"]).cuda()
+    o1, l1 = gpu.fa_fwd(q, k, v, causal=True)
+    d1, dl1 = gpu.fa_decode_paged(dq, kp, vp, bt, sl, 3000)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            a = gpu.fa_fwd(q, k, v, causal=True, stream=s1)
+        with torch.cuda.stream(s2):
+            b = gpu.fa_decode_paged(dq, kp, vp, bt, sl, 3000, stream=s2)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for (o2, l2), (d2, dl2) in outs:
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert torch.equal(d1, d2) and torch.equal(dl1, dl2)
+
+
 def test_empty_keys(gpu):
     q = torch.randn(1, 5, 2, 64, device="cuda").to(torch.bfloat16)
     k = torch.zeros(1, 0, 2, 64, device="cuda", dtype=torch.bfloat16)

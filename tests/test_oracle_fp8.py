@@ -95,6 +95,19 @@ def test_decode_paged_fp8_equals_decode_on_hand_decoded_pools():
     np.testing.assert_array_equal(l3, lse)
 
 
+def test_paged_prefill_fp8_equals_paged_prefill_on_hand_decoded_inputs():
+    c = inputs.paged_prefill_fp8_case(74, [3, 0, 20], [40, 5, 20], 4, 2, 16)
+    ds = tuple(float(x) for x in c["descale"])
+    for causal in (False, True):
+        o, lse = oracle.paged_prefill_fp8(c["q"], c["k_pool"], c["v_pool"], c["block_table"], c["cu_seqlens_q"],
+                                          c["seq_lens"], ds, causal=causal)
+        wid = [torch.from_numpy(c[n]).view(torch.float8_e4m3fn).double().numpy() * f
+               for n, f in zip(("q", "k_pool", "v_pool"), ds)]
+        o2, l2 = oracle.paged_prefill(*wid, c["block_table"], c["cu_seqlens_q"], c["seq_lens"], causal=causal)
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(lse, l2)
+
+
 def test_v_descale_scales_output_only():
     q8, k8, v8, (qd, kd, vd) = _case(72)
     o1, l1 = oracle.fp8_dense(q8, k8, v8, (qd, kd, vd), causal=True)
