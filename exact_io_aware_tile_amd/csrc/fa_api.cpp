@@ -354,40 +354,50 @@ FA_EXPORT fa_status fa_fwd_varlen_fp8(const fa_fwd_varlen_fp8_args* a, void* str
   return ok();
 }
 
-FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
-  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: args is NULL");
+namespace {
+// Chunked prefill over a paged pool: bf16, or FP8 E4M3 queries and pools
+// with descale factors (fp8 != nullptr: q, k, v descales).
+fa_status paged_impl(const fa_fwd_paged_args* a, const float* fp8, const char* fn, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "%s: args is NULL", fn);
   if (a->num_seqs < 0 || a->total_q < 0 || a->max_seqlen_q < 0 || a->max_seqlen_k < 0 || a->heads_q <= 0 ||
       a->heads_kv <= 0 || a->max_blocks_per_seq < 0 || a->num_blocks < 0)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: negative or zero size");
+    return fail(FA_ERR_BAD_SHAPE, "%s: negative or zero size", fn);
   if (a->heads_q % a->heads_kv)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: heads_q (%d) is not a multiple of heads_kv (%d)", a->heads_q,
+    return fail(FA_ERR_BAD_SHAPE, "%s: heads_q (%d) is not a multiple of heads_kv (%d)", fn, a->heads_q,
                 a->heads_kv);
-  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: head_dim %d, supported 64, 128 and 256", a->head_dim);
+  if (fp8 ? a->head_dim != 128 : (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256))
+    return fail(FA_ERR_UNSUPPORTED, "%s: head_dim %d, supported %s", fn, a->head_dim, fp8 ? "128" : "64, 128 and 256");
+  if (fp8)
+    for (int i = 0; i < 3; ++i)
+      if (!(fp8[i] > 0.f) || !std::isfinite(fp8[i]))
+        return fail(FA_ERR_BAD_SHAPE, "%s: descale factors must be positive and finite", fn);
   if (a->block_size != fa::kFwdPagedBlock)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: block_size %d, supported %d", a->block_size,
+    return fail(FA_ERR_UNSUPPORTED, "%s: block_size %d, supported %d", fn, a->block_size,
                 fa::kFwdPagedBlock);
   if ((int64_t)a->max_seqlen_k > (int64_t)a->max_blocks_per_seq * a->block_size)
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: max_seqlen_k %d exceeds max_blocks_per_seq * block_size",
+    return fail(FA_ERR_BAD_SHAPE, "%s: max_seqlen_k %d exceeds max_blocks_per_seq * block_size", fn,
                 a->max_seqlen_k);
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: scale must be positive and finite");
+    return fail(FA_ERR_BAD_SHAPE, "%s: scale must be positive and finite", fn);
   if (a->num_seqs == 0 || a->max_seqlen_q == 0 || a->total_q == 0) return ok();
   if (!a->q || !a->o || !a->cu_seqlens_q || !a->seq_lens_k)
-    return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: q, o, cu_seqlens_q and seq_lens_k are required");
+    return fail(FA_ERR_NULL_POINTER, "%s: q, o, cu_seqlens_q and seq_lens_k are required", fn);
   if (a->max_seqlen_k > 0 && (!a->k_pool || !a->v_pool || !a->block_table))
-    return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged: pools and block_table are required when max_seqlen_k > 0");
-  if (!strides_ok(a->pool_stride, 3, 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: strides must be non-negative multiples of 8 elements");
+    return fail(FA_ERR_NULL_POINTER, "%s: pools and block_table are required when max_seqlen_k > 0", fn);
+  // 16-byte loads and stores: q and pool strides are multiples of 16 bytes
+  // (elements: 8 bf16 or 16 E4M3), o strides of 8 bf16 elements
+  if (!strides_ok(a->pool_stride, 3, fp8 ? 16 : 8) || !strides_ok(a->q_stride, 2, fp8 ? 16 : 8) ||
+      !strides_ok(a->o_stride, 2, 8))
+    return fail(FA_ERR_BAD_SHAPE, "%s: strides must be non-negative multiples of 16 bytes", fn);
   if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->o))
-    return fail(FA_ERR_BAD_SHAPE, "fa_fwd_paged: q, pools and o must be 16-byte aligned");
+    return fail(FA_ERR_BAD_SHAPE, "%s: q, pools and o must be 16-byte aligned", fn);
   if (a->pool_stride[2] > fa::kFwdMaxKvRowStrideBf16)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: pool token stride above %lld elements",
+    return fail(FA_ERR_UNSUPPORTED, "%s: pool token stride above %lld elements", fn,
                 (long long)fa::kFwdMaxKvRowStrideBf16);
-  const int64_t rows = fa::fwd_rows_per_tile_bf16(a->head_dim);
+  const int64_t rows = fp8 ? fa::kFwdRowsPerTileFp8 : fa::fwd_rows_per_tile_bf16(a->head_dim);
   const int64_t qtiles = (a->max_seqlen_q + rows - 1) / rows;
   if (qtiles * a->heads_q * a->num_seqs > 0x7fffffffLL)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_paged: grid too large");
+    return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
 
   fa::FwdParams p{};
   p.q = a->q;
@@ -406,15 +416,28 @@ FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
   p.causal = a->causal ? 1 : 0;
-  p.scale_log2 = scale_log2(a->scale);
+  p.scale_log2 = fp8 ? (float)((double)a->scale * fp8[0] * fp8[1] * 1.4426950408889634073599) : scale_log2(a->scale);
+  p.o_scale = fp8 ? fp8[2] : 1.f;
   p.paged = 1;
   p.block_table = a->block_table;  // with max_seqlen_k == 0 neither table nor pools are read
   p.seq_lens_k = a->seq_lens_k;
   p.max_blocks = a->max_blocks_per_seq;
   p.p_bs = a->pool_stride[0], p.p_hs = a->pool_stride[1], p.p_ts = a->pool_stride[2];
-  const hipError_t e = fa::launch_fwd_bf16(p, a->head_dim, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_paged: launch failed: %s", hipGetErrorString(e));
+  const hipError_t e = fp8 ? fa::launch_fwd_fp8(p, a->head_dim, (hipStream_t)stream)
+                           : fa::launch_fwd_bf16(p, a->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+FA_EXPORT fa_status fa_fwd_paged(const fa_fwd_paged_args* a, void* stream) {
+  return paged_impl(a, nullptr, "fa_fwd_paged", stream);
+}
+
+FA_EXPORT fa_status fa_fwd_paged_fp8(const fa_fwd_paged_fp8_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_fwd_paged_fp8: args is NULL");
+  const float ds[3] = {a->q_descale, a->k_descale, a->v_descale};
+  return paged_impl(&a->base, ds, "fa_fwd_paged_fp8", stream);
 }
 
 namespace {

@@ -69,7 +69,7 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   constexpr int TILE = kBc * D;          // bytes per K or V tile
   constexpr int RPI = 1024 / D;          // rows per 1 KB DMA instruction (8)
@@ -107,7 +107,17 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
 
   int nq, nk;
   int64_t q_base, k_base, v_base, o_base, lse_base;
-  if (p.cu_seqlens) {
+  if (PAGED) {
+    // new queries packed by cu_seqlens; keys of the sequence in the pools
+    const int s0 = p.cu_seqlens[b];
+    nq = p.cu_seqlens[b + 1] - s0;
+    nk = min(max(p.seq_lens_k[b], 0), p.seqlen_k);
+    q_base = (int64_t)s0 * p.q_ss;
+    k_base = 0;
+    v_base = 0;
+    o_base = (int64_t)s0 * p.o_ss;
+    lse_base = (int64_t)h * p.total_tokens + s0;
+  } else if (p.cu_seqlens) {
     const int s0 = p.cu_seqlens[b];
     nq = nk = p.cu_seqlens[b + 1] - s0;
     q_base = (int64_t)s0 * p.q_ss;
@@ -128,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   if (q0 >= nq) return;  // uniform over the workgroup
   const int g = h / p.group;
   q_base += (int64_t)h * p.q_hs;
-  k_base += (int64_t)g * p.k_hs;
-  v_base += (int64_t)g * p.v_hs;
+  k_base += (int64_t)g * (PAGED ? p.p_hs : p.k_hs);
+  v_base += (int64_t)g * (PAGED ? p.p_hs : p.v_hs);
   o_base += (int64_t)h * p.o_hs;
   const int off = nk - nq;  // causal: key j visible from row i iff j <= i + off
 
@@ -176,31 +186,58 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   const int drow = lane / CH;
   const int dpch = lane % CH;
   const int wq = wave & 3;
+  // Paged (an FP8 KV cache): wave w's 16 rows of a tile are exactly one
+  // 16-token pool block, fetched from the block the table names, as in the
+  // bf16 paged instance; the lane offsets are then relative to that block.
+  static_assert(!PAGED || RPW == kFwdPagedBlock, "one pool block per wave and tile");
+  const int64_t kv_row_k = PAGED ? p.p_ts : p.k_ss;
+  const int64_t kv_row_v = PAGED ? p.p_ts : p.v_ss;
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int r = wq * RPW + i * RPI + drow;
-    koff[i] = (uint32_t)((int64_t)r * p.k_ss + swz(r, dpch) * 16);
-    voff[i] = (uint32_t)((int64_t)r * p.v_ss + swz(r, dpch) * 16);
+    const int rs = PAGED ? i * RPI + drow : r;
+    koff[i] = (uint32_t)((int64_t)rs * kv_row_k + swz(r, dpch) * 16);
+    voff[i] = (uint32_t)((int64_t)rs * kv_row_v + swz(r, dpch) * 16);
   }
-  auto dma_one = [&](int tile, bool v_op, int i) {
+  auto wave_block = [&](int tile) {
+    return __builtin_amdgcn_readfirstlane(min(tile * (kBc / kFwdPagedBlock) + wq, (nk - 1) / kFwdPagedBlock));
+  };
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (PAGED ? (int64_t)b * p.max_blocks : 0));
+  auto pool_block = [&](int tile) -> int32_t {
+    if (!PAGED || tile < 0) return 0;
+    return table[wave_block(tile)];
+  };
+  auto dma_one = [&](int tile, bool v_op, int i, int32_t phys) {
     const int st = tile % kStages;
     const int r0 = wq * RPW + i * RPI;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
     const int rows_left = nk - tile * kBc;  // uniform
-    const uint8_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
     uint32_t o = v_op ? voff[i] : koff[i];
-    if (rows_left < kBc) {
-      const int r = r0 + drow;
-      const int rk = min(r, rows_left - 1);
-      o = (uint32_t)((int64_t)rk * (v_op ? p.v_ss : p.k_ss) + swz(r, dpch) * 16);
+    if (PAGED) {
+      if (rows_left < kBc) {
+        const int r = r0 + drow;
+        const int key = tile * kBc + min(r, rows_left - 1);
+        const int rb = key - wave_block(tile) * kFwdPagedBlock;
+        o = (uint32_t)((int64_t)rb * p.p_ts + swz(r, dpch) * 16);
+      }
+      dma_16b((v_op ? vg : kg) + (int64_t)phys * p.p_bs, o, lds);
+    } else {
+      const uint8_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
+      if (rows_left < kBc) {
+        const int r = r0 + drow;
+        const int rk = min(r, rows_left - 1);
+        o = (uint32_t)((int64_t)rk * (v_op ? p.v_ss : p.k_ss) + swz(r, dpch) * 16);
+      }
+      dma_16b(base, o, lds);
     }
-    dma_16b(base, o, lds);
   };
   auto dma_op = [&](int tile, bool v_op) {
+    const int32_t phys = pool_block(tile);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i);
+    for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i, phys);
   };
 
   if (nt > 0) dma_op(0, grp != 0);
@@ -234,13 +271,13 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   i32x8 pf;
   bool corr = false;
   float alpha = 1.f;
-  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v) {
+  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v, int32_t dma_phys) {
     float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       if (dma_tile >= 0 && kc % 2 == 0) {
         __builtin_amdgcn_sched_barrier(0);
-        dma_one(dma_tile, dma_v, kc / 2);
+        dma_one(dma_tile, dma_v, kc / 2, dma_phys);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int kb = kc >> 1;
@@ -258,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
   };
 
-  auto softmax = [&](int t, int dma_tile, bool dma_v) {
+  auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
     if (need_mask) {
@@ -273,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     // Weights against the current reference; a lane sum above 2^8 (or not
     // finite) sends the wave to the exact step (see the bf16 kernel).
     float ps;
-    weights(m_run, ps, dma_tile, dma_v);
+    weights(m_run, ps, dma_tile, dma_v, dma_phys);
     corr = __any(!(ps <= kLazyBound));
     if (corr) {
       float mx[4];
@@ -288,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false, 0);
     }
     l_run += ps;
   };
@@ -347,31 +384,43 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     wait_vmcnt<0>();
     if (nt > 1) dma_op(1, grp != 0);
     lds_barrier();
+    // Paged: the table entry for the DMA of the next softmax phase is read
+    // at the end of the MFMA phase before it (as in the bf16 prefill).
     if (grp == 0) {
       scores(0);
+      int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 2 < nt ? t + 2 : -1, true);
+        softmax(t, t + 2 < nt ? t + 2 : -1, true, ph);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
+        if (PAGED) {
+          __builtin_amdgcn_sched_barrier(0);
+          ph = pool_block(t + 3 < nt ? t + 3 : -1);
+        }
         phase_end(2 * t + 2);
       }
       phase_end(2 * nt + 1);
     } else {
       if (2 < nt) dma_op(2, false);
+      int32_t ph = pool_block(3 < nt ? 3 : -1);
       phase_end(0);
       scores(0);
       phase_end(1);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 3 < nt ? t + 3 : -1, false);
+        softmax(t, t + 3 < nt ? t + 3 : -1, false, ph);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
+        if (PAGED) {
+          __builtin_amdgcn_sched_barrier(0);
+          ph = pool_block(t + 4 < nt ? t + 4 : -1);
+        }
         phase_end(2 * t + 3);
       }
     }
@@ -412,7 +461,10 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
 template <bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int64_t nwg = (int64_t)p.num_qtiles * p.heads_q * p.batch;
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  if (p.paged)
+    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, true>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, false>), dim3((unsigned)nwg), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -97,7 +97,11 @@ class FwdPagedArgs(ctypes.Structure):
                 ("max_blocks_per_seq", _I32), ("num_blocks", _I32), ("scale", _F), ("causal", _I32)]
 
 
-SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_fp8", "fa_fwd_paged", "fa_decode_paged", "fa_decode_paged_workspace_size",
+class FwdPagedFp8Args(ctypes.Structure):
+    _fields_ = [("base", FwdPagedArgs), ("q_descale", _F), ("k_descale", _F), ("v_descale", _F)]
+
+
+SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_fp8", "fa_fwd_paged", "fa_fwd_paged_fp8", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_decode_paged_fp8", "fa_decode_paged_fp8_workspace_size",
            "fa_decode_paged_fp8_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
 
@@ -134,6 +138,8 @@ def lib(path: str = LIB_PATH):
     L.fa_fwd_paged.restype = ctypes.c_int
     L.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
     L.fa_decode_paged.restype = ctypes.c_int
+    L.fa_fwd_paged_fp8.argtypes = [ctypes.POINTER(FwdPagedFp8Args), _P]
+    L.fa_fwd_paged_fp8.restype = ctypes.c_int
     L.fa_decode_paged_fp8.argtypes = [ctypes.POINTER(DecodePagedFp8Args), _P]
     L.fa_decode_paged_fp8.restype = ctypes.c_int
     L.fa_decode_paged_fp8_workspace_size.argtypes = [ctypes.POINTER(DecodePagedFp8Args)]
@@ -497,3 +503,32 @@ def fa_decode_paged_fp8_num_splits(q, k_pool, v_pool, block_table, seq_lens, max
                                    num_splits: int = 0) -> int:
     a = _decode_fp8_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, descale, num_splits)
     return int(lib().fa_decode_paged_fp8_num_splits(ctypes.byref(a)))
+
+
+def fa_fwd_paged_fp8(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q: int,
+                     max_seqlen_k: int, descale, *, causal: bool = True, scale: float | None = None, out=None,
+                     lse=None, return_lse: bool = True, stream=None):
+    """Chunked prefill over an FP8 KV cache: uint8 E4M3 q [Tq, Hq, d] and pools
+    standing for descale[i] * value(code) (q, k, v).  Returns (o, lse), o bf16."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q), ("seq_lens_k", seq_lens_k)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if q.dtype != torch.uint8 or k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise TypeError("fa_fwd_paged_fp8 takes E4M3 q and pools as uint8 tensors")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
+    Tq, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    a = FwdPagedFp8Args()
+    a.base = _fwd_paged_args(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,
+                             causal, scale)
+    a.base.o, a.base.lse = _ptr(out), _ptr(lse)
+    a.base.o_stride[:] = list(out.stride()[:2])
+    a.q_descale, a.k_descale, a.v_descale = (float(x) for x in descale)
+    _check(lib().fa_fwd_paged_fp8(ctypes.byref(a), _stream(stream)))
+    return out, lse

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 typedef enum {
   FA_OK = 0,
@@ -280,6 +280,22 @@ typedef struct {
 } fa_fwd_paged_args;
 
 fa_status fa_fwd_paged(const fa_fwd_paged_args *args, void *stream);
+
+/*
+ * fa_fwd_paged_fp8 -- fa_fwd_paged with FP8 E4M3 queries and pools (an FP8
+ * KV cache) and per-tensor descale factors, computed as fa_fwd_fp8 computes
+ * (both products on the FP8 matrix cores, O normalised by the sum of the
+ * E4M3-rounded weights, LSE by the fp32 sum).  `base` is read as for
+ * fa_fwd_paged with q and the pools as E4M3 codes: their strides count
+ * bytes and are multiples of 16 (o stays bf16, strides in elements).
+ * head_dim 128, block_size 16; descale factors positive and finite.
+ */
+typedef struct {
+  fa_fwd_paged_args base;
+  float q_descale, k_descale, v_descale;
+} fa_fwd_paged_fp8_args;
+
+fa_status fa_fwd_paged_fp8(const fa_fwd_paged_fp8_args *args, void *stream);
 
 /*
  * fa_decode_paged -- one query token per sequence over a paged KV pool

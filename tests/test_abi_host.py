@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 7
+    assert L.fa_abi_version() == declared == 8
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -71,6 +71,7 @@ STRUCTS = {
     "fa_dropout_args": fa.DropoutArgs,
     "fa_fwd_varlen_fp8_args": fa.FwdVarlenFp8Args,
     "fa_decode_paged_fp8_args": fa.DecodePagedFp8Args,
+    "fa_fwd_paged_fp8_args": fa.FwdPagedFp8Args,
 }
 
 
@@ -334,6 +335,25 @@ def test_paged_prefill_rejects_before_launch(L, kw, status):
     a = paged_args(**kw)
     assert L.fa_fwd_paged(ctypes.byref(a), None) == status
     assert L.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,dkw,status", [
+    (dict(head_dim=64), {}, fa.FA_ERR_UNSUPPORTED),
+    (dict(), dict(q_descale=0.0), fa.FA_ERR_BAD_SHAPE),
+    (dict(), dict(v_descale=float("nan")), fa.FA_ERR_BAD_SHAPE),
+    (dict(q_stride=[8 * 128 + 8, 128]), {}, fa.FA_ERR_BAD_SHAPE),   # 8-byte multiple, not 16
+    (dict(heads_q=3), {}, fa.FA_ERR_BAD_SHAPE),
+    (dict(q=None), {}, fa.FA_ERR_NULL_POINTER),
+])
+def test_paged_prefill_fp8_rejects_before_launch(L, kw, dkw, status):
+    a = fa.FwdPagedFp8Args()
+    a.base = paged_args(**kw)
+    a.q_descale = a.k_descale = a.v_descale = 0.01
+    for k, v in dkw.items():
+        setattr(a, k, v)
+    assert L.fa_fwd_paged_fp8(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+    assert L.fa_fwd_paged_fp8(None, None) == fa.FA_ERR_NULL_POINTER
 
 
 def test_paged_prefill_empty_is_noop(L):

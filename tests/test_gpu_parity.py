@@ -717,6 +717,68 @@ def test_paged_prefill_pool_order_bitwise(gpu, d):
     assert torch.equal(l1, l3)
 
 
+def paged_prefill_fp8_gpu(fa, case, causal=True, k_pool=None, v_pool=None, table=None):
+    q = torch.from_numpy(case["q"]).cuda()
+    kp = torch.from_numpy(case["k_pool"]).cuda() if k_pool is None else k_pool
+    vp = torch.from_numpy(case["v_pool"]).cuda() if v_pool is None else v_pool
+    bt = torch.from_numpy(case["block_table"]).cuda() if table is None else table
+    cu = torch.from_numpy(case["cu_seqlens_q"]).cuda()
+    sl = torch.from_numpy(case["seq_lens"]).cuda()
+    o, lse = fa.fa_fwd_paged_fp8(q, kp, vp, bt, cu, sl, case["max_seqlen_q"], int(case["seq_lens"].max(initial=0)),
+                                 case["descale"], causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("group", [1, 4])
+def test_paged_prefill_fp8_parity(gpu, group, causal):
+    case = inputs.paged_prefill_fp8_case(620 + group, PAGED_Q, PAGED_K, 2 * group, 2, 128, pad_blocks=1)
+    o, lse = paged_prefill_fp8_gpu(gpu, case, causal)
+    o_ref, lse_ref = oracle.paged_prefill_fp8(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                              case["cu_seqlens_q"], case["seq_lens"], case["descale"], causal=causal)
+    check_fp8(host(o).transpose(1, 0, 2), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
+              f"fp8 paged prefill group={group} causal={causal}")
+
+
+def test_paged_prefill_fp8_pool_order_bitwise(gpu):
+    q_lens, k_lens = [512, 33, 200], [2000, 33, 1500]
+    case = inputs.paged_prefill_fp8_case(630, q_lens, k_lens, 16, 4, 128)
+    o1, l1 = paged_prefill_fp8_gpu(gpu, case)
+    bt = case["block_table"]
+    order = np.concatenate([bt[b, :(L + 15) // 16] for b, L in enumerate(k_lens)]).astype(np.int64)
+    idx = torch.from_numpy(order).cuda()
+    kp = torch.from_numpy(case["k_pool"]).cuda().index_select(0, idx)
+    vp = torch.from_numpy(case["v_pool"]).cuda().index_select(0, idx)
+    ident = np.full_like(bt, -1)
+    pos = 0
+    for b, L in enumerate(k_lens):
+        nb = (L + 15) // 16
+        ident[b, :nb] = np.arange(pos, pos + nb)
+        pos += nb
+    o2, l2 = paged_prefill_fp8_gpu(gpu, case, k_pool=kp, v_pool=vp, table=torch.from_numpy(ident).cuda())
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_prefill_fp8_whole_context_is_varlen_fp8_bitwise(gpu):
+    lens = [300, 64, 17, 700]
+    case = inputs.paged_prefill_fp8_case(640, lens, lens, 8, 2, 128)
+    o1, l1 = paged_prefill_fp8_gpu(gpu, case)
+    kp, vp = torch.from_numpy(case["k_pool"]).cuda(), torch.from_numpy(case["v_pool"]).cuda()
+    ks, vs = [], []
+    for s_, L in enumerate(lens):
+        t = torch.arange(L, device="cuda")
+        phys = torch.from_numpy(case["block_table"][s_]).cuda().long()[t // 16]
+        ks.append(kp[phys, :, t % 16])
+        vs.append(vp[phys, :, t % 16])
+    k, v = torch.cat(ks).contiguous(), torch.cat(vs).contiguous()
+    cu = torch.from_numpy(case["cu_seqlens_q"]).cuda()
+    o2, l2 = gpu.fa_fwd_varlen_fp8(torch.from_numpy(case["q"]).cuda(), k, v, cu, max(lens), case["descale"],
+                                   causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_paged_prefill_workload_sampled(gpu):
     case = inputs.workload(6)
     T, H = case["total_q"], case["hq"]
