@@ -111,24 +111,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Work item.  Workgroups are dealt round-robin to the 8 XCDs and each
-  // XCD starts them in order as its CUs free up.  When the (sequence, head)
-  // pairs split evenly, XCD x takes a contiguous run of pairs (their K/V stay
-  // in its L2) and starts its items longest first: all pairs' last query
-  // tiles (the heaviest under a causal mask), then the ones before, ...
-  const int nwg = gridDim.x;
-  const int w = blockIdx.x;
-  const int npairs = nwg / p.num_qtiles;
+  // Work item: XCD-balanced, longest first (prefill_work_item).
   int qt, bh;
-  if (npairs % 8 == 0) {
-    const int px = npairs / 8;  // pairs per XCD
-    const int j = w / 8;        // rank of this workgroup on its XCD
-    qt = p.num_qtiles - 1 - j / px;
-    bh = (w % 8) * px + j % px;
-  } else {
-    qt = p.num_qtiles - 1 - (w % p.num_qtiles);
-    bh = w / p.num_qtiles;
-  }
+  prefill_work_item(gridDim.x, blockIdx.x, p.num_qtiles, p.group, qt, bh);
   const int h = bh % p.heads_q;
   const int b = bh / p.heads_q;
 

@@ -90,21 +90,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   const int n = lane & 15;    // the lane's query row (product column)
   const int j = lane >> 4;    // its key group: keys 4j .. 4j+3 of each 16-key block
 
-  // Work item: as in the head_dim 64 / 128 kernel, whole (sequence, head)
-  // runs per XCD, each XCD starting its heaviest causal query tiles first.
-  const int nwg = gridDim.x;
-  const int w = blockIdx.x;
-  const int npairs = nwg / p.num_qtiles;
+  // Work item: XCD-balanced, longest first (prefill_work_item).
   int qt, bh;
-  if (npairs % 8 == 0) {
-    const int px = npairs / 8;
-    const int jj = w / 8;
-    qt = p.num_qtiles - 1 - jj / px;
-    bh = (w % 8) * px + jj % px;
-  } else {
-    qt = p.num_qtiles - 1 - (w % p.num_qtiles);
-    bh = w / p.num_qtiles;
-  }
+  prefill_work_item(gridDim.x, blockIdx.x, p.num_qtiles, p.group, qt, bh);
   const int h = bh % p.heads_q;
   const int b = bh / p.heads_q;
 

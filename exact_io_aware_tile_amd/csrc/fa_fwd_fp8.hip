@@ -86,22 +86,9 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Work item: as in the bf16 prefill, each XCD takes a contiguous run of
-  // (sequence, head) pairs when they split evenly and starts its items
-  // longest first.
-  const int nwg = gridDim.x;
-  const int w = blockIdx.x;
-  const int npairs = nwg / p.num_qtiles;
+  // Work item: XCD-balanced, longest first (prefill_work_item).
   int qt, bh;
-  if (npairs % 8 == 0) {
-    const int px = npairs / 8;
-    const int j = w / 8;
-    qt = p.num_qtiles - 1 - j / px;
-    bh = (w % 8) * px + j % px;
-  } else {
-    qt = p.num_qtiles - 1 - (w % p.num_qtiles);
-    bh = w / p.num_qtiles;
-  }
+  prefill_work_item(gridDim.x, blockIdx.x, p.num_qtiles, p.group, qt, bh);
   const int h = bh % p.heads_q;
   const int b = bh / p.heads_q;
 
