@@ -100,15 +100,21 @@ E4M3_MAX = 448.0
 
 def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
     """Round float32 to FP8 E4M3 codes (uint8): nearest value, ties to the even
-    code, magnitudes above 448 saturated to 448.  Inputs are finite."""
-    a = np.abs(np.asarray(x, dtype=np.float64))
-    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 126)   # first value >= a
-    lo = hi - 1
-    dlo = a - _E4M3_POS[lo]
-    dhi = _E4M3_POS[hi] - a
-    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
-    code = np.where(a >= E4M3_MAX, 126, code).astype(np.uint8)
-    return np.where(np.signbit(np.asarray(x, dtype=np.float32)), code | np.uint8(0x80), code).astype(np.uint8)
+    code, magnitudes above 448 saturated to 448.  Inputs are finite.
+
+    Normal range (|x| >= 2^-6): the float32 mantissa is rounded to 3 bits,
+    ties to even, in integer arithmetic on the bit pattern (a carry moves the
+    exponent); subnormal range: multiples of 2^-9, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    a = np.abs(x)
+    bits = a.view(np.uint32)
+    r = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) & np.uint32(0xFFF00000)
+    e = (r >> np.uint32(23)).astype(np.int32) - (127 - 7)
+    code = (e << 3) | ((r >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
+    sub = a < np.float32(2.0 ** -6)
+    code = np.where(sub, np.rint(a * np.float32(512.0)).astype(np.int32), code)
+    code = np.where(a >= np.float32(E4M3_MAX), 126, np.minimum(code, 126)).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 def e4m3_to_f32(c: np.ndarray) -> np.ndarray:
@@ -118,11 +124,33 @@ def e4m3_to_f32(c: np.ndarray) -> np.ndarray:
     return np.where(c >= 0x80, -v, v)
 
 
+def _chunked(fn, x: np.ndarray, out_dtype):
+    """fn applied to C-order chunks of x (threads: numpy releases the GIL)."""
+    flat = np.ascontiguousarray(x).reshape(-1)
+    out = np.empty(flat.size, dtype=out_dtype)
+    nchunks = (flat.size + CHUNK - 1) // CHUNK
+
+    def run(c: int) -> None:
+        out[c * CHUNK:(c + 1) * CHUNK] = fn(flat[c * CHUNK:(c + 1) * CHUNK])
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            run(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(run, range(nchunks)))
+    return out.reshape(np.shape(x))
+
+
 def to_fp8(x: np.ndarray):
     """Per-tensor scaled E4M3: (codes, descale) with descale = amax / 448."""
-    amax = float(np.max(np.abs(x))) if x.size else 1.0
+    x = np.asarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    starts = range(0, flat.size, CHUNK)
+    with ThreadPoolExecutor(_threads()) as ex:
+        amax = max(ex.map(lambda i: float(np.max(np.abs(flat[i:i + CHUNK]))), starts), default=0.0)
     descale = np.float32(amax / E4M3_MAX if amax > 0 else 1.0)
-    return f32_to_e4m3(np.asarray(x, dtype=np.float32) / descale), descale
+    return _chunked(lambda c: f32_to_e4m3(c / descale), x, np.uint8), descale
 
 
 def _maybe_bf16(x: np.ndarray, dtype: str) -> np.ndarray:
