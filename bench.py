@@ -5,8 +5,10 @@
 
 A step is one fa_fwd call on the headline workload: bf16 causal MHA prefill,
 batch 4, 32 heads, N = 2048, d = 128 (seeded synthetic N(0,1) inputs,
-already resident in HBM).  K steps are timed between barrier +
-synchronisation with HIP events on the launch stream.  The paged GQA decode
+already resident in HBM).  Each workload first runs its step untimed for
+0.3 s (the clock ramps up under sustained load), then W warm-up steps, then
+K steps timed between barrier + synchronisation with HIP events on the
+launch stream.  The paged GQA decode
 workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
 same way and reported in "decode"; the long-context, varlen, chunked paged
 prefill, FP8 prefill, dropout prefill and head_dim 256 prefill workloads are
@@ -93,7 +95,19 @@ def bf16_dev(a, torch, np):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+SETTLE_S = 0.3  # untimed seconds of the same step before the warm-up steps
+
+
 def time_steps(fn, steps, warmup, torch):
+    # The GPU leaves its idle clock only after some time under load (the
+    # inputs are built on the host for seconds before); the same step runs
+    # untimed for SETTLE_S seconds so that the timed steps see the clock of
+    # sustained work, then the W warm-up steps, then exactly K timed steps.
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
