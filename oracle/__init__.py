@@ -62,6 +62,8 @@ def _load(path: str = _LIB):
     lib.oracle_philox4x32_10.restype = None
     lib.oracle_decode_e4m3.argtypes = [P, P, I64]
     lib.oracle_decode_e4m3.restype = None
+    lib.oracle_merge_states.argtypes = [I64, I64, I64, P, P, P, P]
+    lib.oracle_merge_states.restype = None
     for f in (lib.oracle_attn_dense, lib.oracle_attn_varlen, lib.oracle_attn_decode_paged,
               lib.oracle_attn_paged_prefill, lib.oracle_max_threads):
         f.restype = I
@@ -379,4 +381,24 @@ def varlen_dropout(q, k, v, cu_seqlens, *, causal: bool, dropout_p: float, seed:
         raise ValueError(f"oracle_attn_varlen_dropout failed with status {st}")
     if r is None:
         return o.reshape(Hq, T, d), lse.reshape(Hq, T)
+    return o, lse
+
+
+def merge_states(o_parts, lse_parts, *, lib=None):
+    """Merge P attention results of the same rows over disjoint key sets
+    ("FlashAttention", tachyon.techntrek.in, "For engineers / Show the
+    maths", the (m, l, o) merge rule over P states): o_parts [P, ..., d]
+    (bf16 bit patterns as uint16, or floats) and lse_parts [P, ...] (natural
+    log, -inf = the part saw no key) -> (o [..., d], lse [...]) in fp64."""
+    lib = lib or _load()
+    o_parts = np.ascontiguousarray(_widen(o_parts))
+    lse_parts = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+    P, d = o_parts.shape[0], o_parts.shape[-1]
+    rows_shape = o_parts.shape[1:-1]
+    if lse_parts.shape != (P,) + rows_shape:
+        raise ValueError(f"lse_parts {lse_parts.shape} does not match o_parts {o_parts.shape}")
+    R = int(np.prod(rows_shape, dtype=np.int64))
+    o = np.zeros(rows_shape + (d,), dtype=np.float64)
+    lse = np.zeros(rows_shape, dtype=np.float64)
+    lib.oracle_merge_states(P, R, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse))
     return o, lse

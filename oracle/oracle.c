@@ -533,3 +533,40 @@ int oracle_attn_paged_prefill(const void *q, const void *kpool, const void *vpoo
   }
   return bad;
 }
+
+/*
+ * Merge of P partial attention results of the same R query rows over
+ * disjoint key sets ("FlashAttention", tachyon.techntrek.in, "For engineers /
+ * Show the maths": two states (m, l, o) combine by rescaling both to the
+ * larger max and adding; here all P states at once).  Part p gives its
+ * normalised output o_p (d values per row) and lse_p = m_p + log l_p; against
+ * m = max_p lse_p part p weighs w_p = exp(lse_p - m) = l_p exp(m_p - m), and
+ * the union is o = sum_p w_p o_p / sum_p w_p, lse = m + log sum_p w_p.  A part
+ * with lse_p = -inf saw no key for that row and is skipped (its o_p is not
+ * read); a row no part saw gets o = 0, lse = -inf.
+ * Layouts: o_parts [P][R][d], lse_parts [P][R], o [R][d], lse [R].
+ */
+void oracle_merge_states(int64_t P, int64_t R, int64_t d, const double *o_parts, const double *lse_parts,
+                         double *o, double *lse) {
+  for (int64_t r = 0; r < R; ++r) {
+    double m = -INFINITY;
+    for (int64_t p = 0; p < P; ++p)
+      if (lse_parts[p * R + r] > m) m = lse_parts[p * R + r];
+    double *orow = o + r * d;
+    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+    if (m == -INFINITY) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double z = 0.0;
+    for (int64_t p = 0; p < P; ++p) {
+      const double lp = lse_parts[p * R + r];
+      if (lp == -INFINITY) continue;
+      const double w = exp(lp - m);
+      z += w;
+      for (int64_t c = 0; c < d; ++c) orow[c] += w * o_parts[(p * R + r) * d + c];
+    }
+    for (int64_t c = 0; c < d; ++c) orow[c] /= z;
+    lse[r] = m + log(z);
+  }
+}

@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle_dropout as DR
 from tests import test_oracle_fp8 as F
+from tests import test_oracle_merge as M
 from tests import test_oracle_paged_prefill as C
 from tests import test_oracle_pins as P
 from tests import test_recurrence_cpu as R
@@ -68,6 +69,12 @@ MUTANTS = {
                                "(uint32_t)((uint64_t)dp->row >> 32),\n                           0u}"),
     "dropout dense row layout": ("dp.row = id; /* (b * Hq + h) * Nq + i */", "dp.row = (h * B + b) * Nq + i;"),
     "dropout packed row layout": ("dp.row = id; /* h * T + t */", "dp.row = t * Hq + h;"),
+    "merge lse drops max": ("lse[r] = m + log(z);", "lse[r] = log(z);"),
+    "merge unnormalised": ("for (int64_t c = 0; c < d; ++c) orow[c] /= z;", "(void)z;"),
+    "merge first part skipped": ("for (int64_t p = 0; p < P; ++p) {\n      const double lp",
+                                 "for (int64_t p = 1; p < P; ++p) {\n      const double lp"),
+    "merge weight sign": ("const double w = exp(lp - m);", "const double w = exp(m - lp);"),
+    "merge parts transposed": ("o_parts[(p * R + r) * d + c]", "o_parts[(r * P + p) * d + c]"),
 }
 
 PINS = [
@@ -98,6 +105,11 @@ PINS = [
     (DR.test_keep_rate_and_unbiased_scaling, {}),
     (DR.test_single_packed_sequence_numbers_rows_like_dense, {}),
     (DR.test_packed_keep_decisions_use_head_major_rows_and_local_keys, {}),
+    (M.test_key_partition_reaches_full_attention, {}),
+    (M.test_causal_ring_chunks_merge_to_causal_attention, {}),
+    (M.test_worked_example_as_two_parts, {}),
+    (M.test_matches_pairwise_recurrence_merge, {}),
+    (M.test_special_cases, {}),
 ]
 
 
