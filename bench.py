@@ -13,8 +13,9 @@ workload (batch 64, 32/8 heads, d = 128, lengths U{1024..32768}) is timed the
 same way and reported in "decode"; the long-context, varlen, chunked paged
 prefill, FP8 prefill, dropout prefill and head_dim 256 prefill workloads are
 reported in "extra" (FP8 against the 5.0 PFLOP/s dense fp8 peak), as is a
-head_dim 256 paged decode workload and the paged decode workload over an FP8
-KV cache (GB/s).
+head_dim 256 paged decode workload, the paged decode workload over an FP8
+KV cache and the merge of 8 key-shard results of the long-context shape
+(GB/s).
 
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
@@ -47,6 +48,7 @@ KERNEL_SOURCES = {
     "varlen": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "decode_d256": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
     "decode_fp8": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
+    "merge": ["exact_io_aware_tile_amd/csrc/fa_merge.hip"],
 }
 
 
@@ -61,7 +63,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", nargs="+", choices=["prefill", "decode", "long", "varlen", "chunked", "fp8", "dropout",
-                                                 "d256", "decode_d256", "decode_fp8", "copy"],
+                                                 "d256", "decode_d256", "decode_fp8", "merge", "copy"],
                     default=None,
                     help="run only these workloads and print one JSON line each (for profiler "
                          "runs); 'copy' runs a plain 1 GiB device copy used to calibrate the "
@@ -332,6 +334,27 @@ def run_decode(fa, case, steps, warmup, torch, np, flush=None, kind="decode"):
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}}
 
 
+def run_merge(fa, case, steps, warmup, torch, np):
+    """Merge of P key-shard results: algorithmic bytes = P x (output rows +
+    their lse) read + one output (rows + lse) written."""
+    o_parts = bf16_dev(case["o_parts"], torch, np)
+    lse_parts = torch.from_numpy(case["lse_parts"]).cuda()
+    P, B, S, H, D = case["o_parts"].shape
+    o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.fa_merge_states(o_parts, lse_parts, out=o, lse=lse)
+
+    ms, _ = time_steps(step, steps, warmup, torch)
+    rows = B * S * H
+    nbytes = float((P + 1) * rows * (2 * D + 4))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "gbs": gbs, "bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("merge")}}
+
+
 def run_copy(torch, steps):
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -400,6 +423,9 @@ def main():
     if want("decode_fp8", not args.no_extra):
         case = inputs.workload(11)
         out["decode_fp8"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, kind="decode_fp8"))
+    if want("merge", not args.no_extra):
+        case = inputs.workload(12)
+        out["merge"] = (case, run_merge(fa, case, args.steps, args.warmup, torch, np))
     if want("decode", not args.no_decode):
         case = inputs.workload(5)
         out["decode"] = (case, run_decode(fa, case, args.steps, args.warmup, torch, np, flush))
@@ -442,7 +468,7 @@ def main():
         flush = None
         line["decode"]["copy_gbs"] = round(copy_bandwidth(torch), 1)
     extra = []
-    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256", "decode_d256", "decode_fp8"):
+    for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256", "decode_d256", "decode_fp8", "merge"):
         if key in out:
             c, r = out[key]
             if "gbs" in r:

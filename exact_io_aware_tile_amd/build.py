@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa_gfx950.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_bf16_d256.hip", "fa_fwd_fp8.hip", "fa_fwd_f32.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_bf16_d256.hip", "fa_fwd_fp8.hip", "fa_fwd_f32.hip", "fa_decode.hip", "fa_merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -540,6 +540,39 @@ FA_EXPORT fa_status fa_decode_paged_fp8(const fa_decode_paged_fp8_args* a, void*
   return decode_impl(&a->base, true, a->k_descale, a->v_descale, "fa_decode_paged_fp8", stream);
 }
 
+FA_EXPORT fa_status fa_merge_states(const fa_merge_states_args* a, void* stream) {
+  if (!a) return fail(FA_ERR_NULL_POINTER, "fa_merge_states: args is NULL");
+  if (a->num_parts < 1 || a->batch < 0 || a->seqlen < 0 || a->heads < 0)
+    return fail(FA_ERR_BAD_SHAPE, "fa_merge_states: num_parts must be >= 1 and sizes >= 0");
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256)
+    return fail(FA_ERR_UNSUPPORTED, "fa_merge_states: head_dim %d (supported: 64, 128, 256)", a->head_dim);
+  if (a->dtype != FA_BF16 && a->dtype != FA_F32)
+    return fail(FA_ERR_UNSUPPORTED, "fa_merge_states: dtype %d", (int)a->dtype);
+  const int64_t rows = (int64_t)a->batch * a->seqlen * a->heads;
+  if (rows == 0) return ok();
+  if ((double)a->num_parts * (double)rows * a->head_dim >= 1099511627776.0)
+    return fail(FA_ERR_UNSUPPORTED, "fa_merge_states: more than 2^40 input elements");
+  if (!a->o_parts || !a->lse_parts || !a->o) return fail(FA_ERR_NULL_POINTER, "fa_merge_states: NULL tensor");
+  if (!aligned16(a->o_parts) || !aligned16(a->lse_parts) || !aligned16(a->o) || (a->lse && !aligned16(a->lse)))
+    return fail(FA_ERR_BAD_SHAPE, "fa_merge_states: pointers must be 16-byte aligned");
+  fa::MergeParams p{};
+  p.o_parts = a->o_parts;
+  p.lse_parts = a->lse_parts;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.rows = rows;
+  p.part_elems = rows * a->head_dim;
+  p.part_rows = rows;
+  p.parts = a->num_parts;
+  p.seqlen = a->seqlen;
+  p.heads = a->heads;
+  p.head_dim = a->head_dim;
+  p.f32 = a->dtype == FA_F32;
+  const hipError_t e = fa::launch_merge(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_merge_states: %s", hipGetErrorString(e));
+  return ok();
+}
+
 FA_EXPORT const char* fa_status_string(fa_status status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -103,4 +103,18 @@ hipError_t launch_decode_paged(const DecodeParams& p, int head_dim, hipStream_t 
 int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim, bool kv8);
 size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim);
 
+// Merge of P partial (o, lse) states of the same rows.
+struct MergeParams {
+  const void* o_parts;    // [parts][rows][head_dim], bf16 or fp32
+  const float* lse_parts; // [parts][batch][heads][seqlen]
+  void* o;                // [rows][head_dim]
+  float* lse;             // [batch][heads][seqlen] or null
+  int64_t rows;           // batch * seqlen * heads, in that (row-major) order
+  int64_t part_elems;     // rows * head_dim
+  int64_t part_rows;      // rows
+  int32_t parts, seqlen, heads, head_dim;
+  int32_t f32;
+};
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
 }  // namespace fa

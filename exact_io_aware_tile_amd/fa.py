@@ -101,9 +101,14 @@ class FwdPagedFp8Args(ctypes.Structure):
     _fields_ = [("base", FwdPagedArgs), ("q_descale", _F), ("k_descale", _F), ("v_descale", _F)]
 
 
+class MergeStatesArgs(ctypes.Structure):
+    _fields_ = [("num_parts", _I32), ("batch", _I32), ("seqlen", _I32), ("heads", _I32), ("head_dim", _I32),
+                ("dtype", ctypes.c_int), ("o_parts", _P), ("lse_parts", _P), ("o", _P), ("lse", _P)]
+
+
 SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_fp8", "fa_fwd_paged", "fa_fwd_paged_fp8", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_decode_paged_fp8", "fa_decode_paged_fp8_workspace_size",
-           "fa_decode_paged_fp8_num_splits", "fa_status_string", "fa_last_error", "fa_abi_version")
+           "fa_decode_paged_fp8_num_splits", "fa_merge_states", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -150,6 +155,8 @@ def lib(path: str = LIB_PATH):
     L.fa_decode_paged_workspace_size.restype = ctypes.c_size_t
     L.fa_decode_paged_num_splits.argtypes = [ctypes.POINTER(DecodePagedArgs)]
     L.fa_decode_paged_num_splits.restype = _I32
+    L.fa_merge_states.argtypes = [ctypes.POINTER(MergeStatesArgs), _P]
+    L.fa_merge_states.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -531,4 +538,27 @@ def fa_fwd_paged_fp8(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, m
     a.base.o_stride[:] = list(out.stride()[:2])
     a.q_descale, a.k_descale, a.v_descale = (float(x) for x in descale)
     _check(lib().fa_fwd_paged_fp8(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def fa_merge_states(o_parts, lse_parts, *, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Merge P results over disjoint key sets: o_parts [P, B, S, H, D] and
+    lse_parts [P, B, H, S] (contiguous) -> (o [B, S, H, D], lse [B, H, S])."""
+    torch = _torch()
+    _dev(o_parts, lse_parts, out, lse)
+    if o_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise ValueError("o_parts must be [P, B, S, H, D] and lse_parts [P, B, H, S]")
+    P, B, S, H, D = o_parts.shape
+    if tuple(lse_parts.shape) != (P, B, H, S) or lse_parts.dtype != torch.float32:
+        raise ValueError(f"lse_parts must be fp32 {(P, B, H, S)}, got {tuple(lse_parts.shape)} {lse_parts.dtype}")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=o_parts.dtype, device=o_parts.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    if not out.is_contiguous() or tuple(out.shape) != (B, S, H, D) or out.dtype != o_parts.dtype:
+        raise ValueError("out must be a contiguous [B, S, H, D] tensor of o_parts' dtype")
+    a = MergeStatesArgs(P, B, S, H, D, _dtype_code(o_parts), _ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse))
+    _check(lib().fa_merge_states(ctypes.byref(a), _stream(stream)))
     return out, lse

@@ -314,6 +314,28 @@ def paged_prefill_fp8_case(seed: int, q_lens, k_lens, hq: int, hkv: int, d: int,
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------
+# --------------------------------------------------------------------------
+# partial results to merge: o_parts [P, B, S, H, d], lse_parts [P, B, H, S]
+# --------------------------------------------------------------------------
+def merge_case(seed: int, parts: int, batch: int, seqlen: int, heads: int, d: int, dtype: str = "bf16",
+               empty_frac: float = 0.0) -> dict:
+    """Seeded partial attention results of the same rows over ``parts`` key
+    shards: outputs N(0, 0.3^2) (a normalised output is a convex combination
+    of value rows), log-sum-exps 4 + N(0, 2^2) (shards of a few hundred keys
+    whose max scores differ by a few units).  A fraction ``empty_frac`` of
+    (part, row) entries is marked as a shard that saw no key: lse -inf and
+    an output row of NaN, which a merge must ignore."""
+    o = normal_f32(seed, 201, (parts, batch, seqlen, heads, d)) * np.float32(0.3)
+    lse = normal_f32(seed, 202, (parts, batch, heads, seqlen)) * np.float32(2.0) + np.float32(4.0)
+    if empty_frac > 0.0:
+        rng = np.random.default_rng([seed, 203])
+        empty = rng.random((parts, batch, heads, seqlen)) < empty_frac
+        lse[empty] = -np.inf
+        o[np.transpose(empty, (0, 1, 3, 2))] = np.nan
+    return {"o_parts": _maybe_bf16(o, dtype), "lse_parts": lse, "dtype": dtype, "parts": parts,
+            "batch": batch, "seqlen": seqlen, "heads": heads, "d": d}
+
+
 def workload(n: int) -> dict:
     """The five synthetic workloads (seed = workload number):
 
@@ -334,7 +356,10 @@ def workload(n: int) -> dict:
     at head_dim 256, batch 2, 16 q heads / 8 kv heads, N = 4096 (the shape of
     a head_dim-256 model's prefill); 10. bf16 paged GQA decode at head_dim
     256, batch 32, 16 q heads / 8 kv heads, lengths U{1024..16384}; 11.
-    workload 5 with an FP8 E4M3 KV cache (per-tensor descale amax/448).
+    workload 5 with an FP8 E4M3 KV cache (per-tensor descale amax/448); 12.
+    the merge of 8 key-shard results of workload 3's shape (batch 1,
+    N = 8192, 32 heads, d = 128, bf16): what each GPU of an 8-way ring over
+    the keys merges for its queries.
     """
     if n == 1:
         c = dense_case(1, 1, 256, 256, 1, 1, 64, dtype="f32")
@@ -380,6 +405,10 @@ def workload(n: int) -> dict:
     if n == 7:
         c = fp8_case(7, 4, 2048, 2048, 32, 32, 128)
         c.update(causal=True, name="fp8 e4m3 causal MHA prefill B=4 H=32 N=2048 d=128")
+        return c
+    if n == 12:
+        c = merge_case(12, 8, 1, 8192, 32, 128, dtype="bf16")
+        c.update(name="merge of 8 key-shard results B=1 N=8192 H=32 d=128 bf16")
         return c
     if n == 6:
         k_lens = varlen_lengths(6, 16, 1024, 8192)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
 
 typedef enum {
   FA_OK = 0,
@@ -386,6 +386,47 @@ typedef struct {
 fa_status fa_decode_paged_fp8(const fa_decode_paged_fp8_args *args, void *stream);
 size_t fa_decode_paged_fp8_workspace_size(const fa_decode_paged_fp8_args *args);
 int32_t fa_decode_paged_fp8_num_splits(const fa_decode_paged_fp8_args *args);
+
+/*
+ * fa_merge_states -- merge the results of attention of the same queries
+ * over P disjoint key sets into the result over their union.  Each part p
+ * gives, per query row, its normalised output o_p and its log-sum-exp
+ * lse_p (the forms every entry point above writes); with m = max_p lse_p
+ * and w_p = exp(lse_p - m), the union has
+ *     o = sum_p w_p o_p / sum_p w_p,   lse = m + log(sum_p w_p).
+ * This is the (m, l, o) merge rule of "FlashAttention"
+ * (tachyon.techntrek.in), "For engineers / Show the maths", applied once
+ * to P states; "S12 FlashAttention" (llminference.xinbetween.com), "What
+ * this unlocks beyond speed", uses it to pass one sequence's keys around a
+ * ring of GPUs and to combine flash-decoding splits across processors.
+ * The key sets may live on other devices: gather their (o_p, lse_p) here
+ * and merge once.
+ *
+ *   num_parts P >= 1; batch, seqlen, heads >= 0; head_dim in {64, 128, 256}.
+ *   dtype: FA_BF16 or FA_F32, for o_parts and o alike.
+ *   o_parts: DEVICE [P, batch, seqlen, heads, head_dim] contiguous (part p
+ *       starts at element p * batch * seqlen * heads * head_dim).
+ *   lse_parts: DEVICE fp32 [P, batch, heads, seqlen] contiguous, natural
+ *       log.  -inf marks a row for which part p saw no key: its o_p row is
+ *       then not read.  Values must not be NaN or +inf.
+ *   o: DEVICE [batch, seqlen, heads, head_dim] contiguous (written); must not
+ *       overlap the inputs.
+ *   lse: DEVICE fp32 [batch, heads, seqlen] (written; may be NULL).
+ * A row with lse_p = -inf in every part gets o = 0 and lse = -inf.  The
+ * dense (seqlen = N), packed (batch = 1, seqlen = total tokens) and decode
+ * (seqlen = 1) outputs all have this layout.  All pointers 16-byte
+ * aligned; P * batch * seqlen * heads * head_dim below 2^40.
+ */
+typedef struct {
+  int32_t num_parts, batch, seqlen, heads, head_dim;
+  fa_dtype dtype;
+  const void *o_parts;
+  const float *lse_parts;
+  void *o;
+  float *lse;
+} fa_merge_states_args;
+
+fa_status fa_merge_states(const fa_merge_states_args *args, void *stream);
 
 /* Static text for a status code. */
 const char *fa_status_string(fa_status status);

@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 8
+    assert L.fa_abi_version() == declared == 9
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -72,6 +72,7 @@ STRUCTS = {
     "fa_fwd_varlen_fp8_args": fa.FwdVarlenFp8Args,
     "fa_decode_paged_fp8_args": fa.DecodePagedFp8Args,
     "fa_fwd_paged_fp8_args": fa.FwdPagedFp8Args,
+    "fa_merge_states_args": fa.MergeStatesArgs,
 }
 
 
@@ -480,3 +481,37 @@ def test_binding_refuses_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(fa, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         fa.lib(str(tmp_path / "missing.so"))
+
+
+def merge_args(**kw):
+    d = dict(num_parts=2, batch=1, seqlen=5, heads=3, head_dim=128, dtype=fa.FA_BF16, o_parts=0x1000,
+             lse_parts=0x2000, o=0x3000, lse=0x4000)
+    d.update(kw)
+    return fa.MergeStatesArgs(*(d[f] for f, _ in fa.MergeStatesArgs._fields_))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_parts=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(batch=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(heads=-2), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(o_parts=None), fa.FA_ERR_NULL_POINTER),
+    (dict(lse_parts=None), fa.FA_ERR_NULL_POINTER),
+    (dict(o=None), fa.FA_ERR_NULL_POINTER),
+    (dict(o=0x3008), fa.FA_ERR_BAD_SHAPE),
+    (dict(lse=0x4004), fa.FA_ERR_BAD_SHAPE),
+    (dict(num_parts=1 << 20, batch=1 << 10, seqlen=1 << 10), fa.FA_ERR_UNSUPPORTED),
+])
+def test_merge_rejects_before_launch(L, kw, status):
+    a = merge_args(**kw)
+    assert L.fa_merge_states(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_merge_empty_is_noop(L):
+    for kw in (dict(batch=0), dict(seqlen=0), dict(heads=0)):
+        a = merge_args(o_parts=None, lse_parts=None, o=None, lse=None, **kw)
+        assert L.fa_merge_states(ctypes.byref(a), None) == fa.FA_OK
+        assert L.fa_last_error() == b""
+    assert L.fa_merge_states(None, None) == fa.FA_ERR_NULL_POINTER
