@@ -16,7 +16,7 @@
 // so a wave covers whole rows with fully coalesced, non-temporal loads (each
 // input byte is read once).  The row's P log-sum-exps are read by all of its
 // lanes at the same address and served by one cache line.  Parts are
-// unrolled by four so several loads are in flight per lane.
+// taken eight at a time in one pass, all eight loads in flight together.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -24,6 +24,11 @@ namespace fa {
 namespace {
 
 constexpr int kMergeThreads = 256;
+constexpr int kGroup = 8;  // parts whose loads are in flight together
+#ifndef FA_MERGE_MAX_GRID
+#define FA_MERGE_MAX_GRID 65536
+#endif
+constexpr int64_t kMergeMaxGrid = FA_MERGE_MAX_GRID;  // workgroups; the rest is a grid-stride loop
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -62,24 +67,46 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     const int64_t li = (b * p.heads + h) * p.seqlen + s;  // [batch, heads, seqlen] order
     const int64_t e = r * D + 8 * c;
 
+    // One pass over the parts in groups of kGroup: a group's loads (its
+    // log-sum-exps and output rows) are all issued before any is used, the
+    // group's max moves the running reference m, and what was accumulated
+    // against the old reference is rescaled by exp(m_old - m_new) -- the
+    // pages' own recurrence, with states in place of key tiles.  Past the
+    // last part the index is clamped to it (a valid address) and the part
+    // counts as empty.
     float m = -INFINITY;
-    for (int q = 0; q < p.parts; ++q) m = fmaxf(m, p.lse_parts[q * p.part_rows + li]);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float sw = 0.f;
-    if (m != -INFINITY) {
-#pragma unroll 4
-      for (int q = 0; q < p.parts; ++q) {
-        const float lq = p.lse_parts[q * p.part_rows + li];
-        float x[8];
-        load8<F32>(p.o_parts, q * p.part_elems + e, x);
+    for (int q0 = 0; q0 < p.parts; q0 += kGroup) {
+      float lq[kGroup];
+      float x[kGroup][8];
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        const int64_t q = min(q0 + u, p.parts - 1);
+        lq[u] = p.lse_parts[q * p.part_rows + li];
+        if (q0 + u >= p.parts) lq[u] = -INFINITY;
+        load8<F32>(p.o_parts, q * p.part_elems + e, x[u]);
+      }
+      float gm = lq[0];
+#pragma unroll
+      for (int u = 1; u < kGroup; ++u) gm = fmaxf(gm, lq[u]);
+      if (gm == -INFINITY) continue;  // no part of the group saw a key of this row
+      const float m_new = fmaxf(m, gm);
+      const float a = exp2f((m - m_new) * kLog2e);  // 0 while nothing was accumulated (m = -inf)
+      sw *= a;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= a;
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
         // A part that saw no key (lse -inf) contributes nothing, whatever
         // its output row holds.
-        const bool live = lq != -INFINITY;
-        const float w = live ? exp2f((lq - m) * kLog2e) : 0.f;
+        const bool live = lq[u] != -INFINITY;
+        const float w = live ? exp2f((lq[u] - m_new) * kLog2e) : 0.f;
         sw += w;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += live ? w * x[j] : 0.f;
+        for (int j = 0; j < 8; ++j) acc[j] += live ? w * x[u][j] : 0.f;
       }
+      m = m_new;
     }
     // sw >= 1: the part that holds the max weighs exactly 1.
     const float inv = m != -INFINITY ? 1.f / sw : 0.f;
@@ -103,7 +130,7 @@ template <int D>
 hipError_t launch_merge_d(const MergeParams& p, hipStream_t stream) {
   const int64_t n = p.rows * (D / 8);
   const int64_t blocks = (n + kMergeThreads - 1) / kMergeThreads;
-  const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+  const unsigned grid = (unsigned)(blocks < kMergeMaxGrid ? blocks : kMergeMaxGrid);
   if (p.f32)
     merge_kernel<D, true><<<grid, kMergeThreads, 0, stream>>>(p);
   else
