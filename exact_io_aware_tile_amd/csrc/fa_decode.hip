@@ -461,17 +461,41 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
     const int64_t row0 = (int64_t)h * S + b;
     // Parts with an empty range (possible when U < P) hold no piece.
     auto empty = [&](int w) { return (int64_t)w * U / P == (int64_t)(w + 1) * U / P; };
-    for (int w = w0; w <= w1; ++w)
-      if (!empty(w)) M = fmaxf(M, p.ws_ml[(row0 + w) * kMlStride]);
-    for (int w = w0; w <= w1; ++w) {
-      if (empty(w)) continue;
-      const float4 ml = *(const float4*)(p.ws_ml + (row0 + w) * kMlStride);
-      const float wt = exp2_fast(ml.x - M);
-      l = __builtin_fmaf(wt, ml.y, l);
-      lb = __builtin_fmaf(wt, ml.z, lb);
-      const float* v = p.ws_o + (row0 + w) * kD + DPL * lane;
+    // One pass over the pieces, four at a time with all their loads issued
+    // together: the group's max moves the reference M and what was merged
+    // so far is rescaled by 2^(M_old - M_new).  Past w1 the index is clamped
+    // (a valid address) and, like an empty part, the piece is dead; a dead
+    // piece's workspace row is never used (it may hold anything).
+    for (int w = w0; w <= w1; w += 4) {
+      float4 ml[4];
+      float v[4][DPL];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) oa[i] = __builtin_fmaf(wt, v[i], oa[i]);
+      for (int u = 0; u < 4; ++u) {
+        const int wu = min(w + u, w1);
+        ml[u] = *(const float4*)(p.ws_ml + (row0 + wu) * kMlStride);
+        const float* src = p.ws_o + (row0 + wu) * kD + DPL * lane;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) v[u][i] = src[i];
+        if (w + u > w1 || empty(w + u)) ml[u].x = -INFINITY;
+      }
+      const float gm = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
+      if (gm == -INFINITY) continue;
+      const float Mn = fmaxf(M, gm);
+      const float a = exp2_fast(M - Mn);  // 0 while nothing was merged (M = -inf)
+      l *= a;
+      lb *= a;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) oa[i] *= a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool live = ml[u].x != -INFINITY;
+        const float wt = live ? exp2_fast(ml[u].x - Mn) : 0.f;
+        l = __builtin_fmaf(wt, ml[u].y, l);
+        lb = __builtin_fmaf(wt, ml[u].z, lb);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) oa[i] = live ? __builtin_fmaf(wt, v[u][i], oa[i]) : oa[i];
+      }
+      M = Mn;
     }
   }
   // o / lb: the weights P.V used, so the row is a convex combination of
