@@ -50,6 +50,18 @@ float scale_log2(float scale) { return (float)((double)scale * 1.442695040888963
 
 constexpr int kDecodeBlock = 16;
 
+// Pairs per chunk of the prefill work mapping: whole GQA groups, as many as
+// keep their K/V (at the longest length) within one XCD's 4 MB L2.  Below
+// four pairs a chunk is too small to balance its causal items and the plain
+// order (0) is used: measured on MI355X, the chunked order cuts the K/V
+// re-reads of packed and chunked-paged prefill several-fold and is a few
+// percent faster there and at B=4 N=2048, and slower with one pair per chunk.
+int32_t wi_chunk(int max_seqlen, int head_dim, int elem_bytes, int group) {
+  const double kv = 2.0 * (double)max_seqlen * head_dim * elem_bytes;  // K and V of one kv head
+  const double c = std::floor((4 << 20) / (kv > 1.0 ? kv : 1.0)) * group;
+  return c < 4.0 ? 0 : c > 65536.0 ? 65536 : (int32_t)c;  // 65536 or more pairs: one chunk, the plain order
+}
+
 fa_status check_decode(const fa_decode_paged_args* a) {
   if (!a) return fail(FA_ERR_NULL_POINTER, "fa_decode_paged: args is NULL");
   if (a->batch < 0 || a->heads_q <= 0 || a->heads_kv <= 0 || a->max_seq_len < 0 ||
@@ -157,6 +169,7 @@ fa_status fwd_dense(const fa_fwd_args* a, const fa_dropout_args* drop, const cha
   p.heads_q = a->heads_q;
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
+  p.wi_chunk = wi_chunk(a->seqlen_k, a->head_dim, a->dtype == FA_BF16 ? 2 : 4, p.group);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = scale_log2(a->scale);
   hipStream_t s = (hipStream_t)stream;
@@ -218,6 +231,7 @@ fa_status fwd_varlen(const fa_fwd_varlen_args* a, const fa_dropout_args* drop, c
   p.heads_q = a->heads_q;
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
+  p.wi_chunk = wi_chunk(a->max_seqlen, a->head_dim, a->dtype == FA_BF16 ? 2 : 4, p.group);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = scale_log2(a->scale);
   hipStream_t s = (hipStream_t)stream;
@@ -291,6 +305,7 @@ FA_EXPORT fa_status fa_fwd_fp8(const fa_fwd_fp8_args* a, void* stream) {
   p.heads_q = a->heads_q;
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
+  p.wi_chunk = wi_chunk(a->seqlen_k, a->head_dim, 1, p.group);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = (float)((double)a->scale * a->q_descale * a->k_descale * 1.4426950408889634073599);
   p.o_scale = a->v_descale;
@@ -346,6 +361,7 @@ FA_EXPORT fa_status fa_fwd_varlen_fp8(const fa_fwd_varlen_fp8_args* a, void* str
   p.heads_q = a->heads_q;
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
+  p.wi_chunk = wi_chunk(a->max_seqlen, a->head_dim, 1, p.group);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = (float)((double)a->scale * a->q_descale * a->k_descale * 1.4426950408889634073599);
   p.o_scale = a->v_descale;
@@ -415,6 +431,7 @@ fa_status paged_impl(const fa_fwd_paged_args* a, const float* fp8, const char* f
   p.heads_q = a->heads_q;
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
+  p.wi_chunk = wi_chunk(a->max_seqlen_k, a->head_dim, fp8 ? 1 : 2, p.group);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = fp8 ? (float)((double)a->scale * fp8[0] * fp8[1] * 1.4426950408889634073599) : scale_log2(a->scale);
   p.o_scale = fp8 ? fp8[2] : 1.f;

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
 
   // Work item: XCD-balanced, longest first (prefill_work_item).
   int qt, bh;
-  prefill_work_item(gridDim.x, blockIdx.x, p.num_qtiles, p.group, qt, bh);
+  prefill_work_item(gridDim.x, blockIdx.x, p.num_qtiles, p.group, p.wi_chunk, qt, bh);
   const int h = bh % p.heads_q;
   const int b = bh / p.heads_q;
 

@@ -60,6 +60,9 @@ struct FwdParams {
   int32_t drop_t;
   uint32_t drop_seed_lo, drop_seed_hi, drop_offset;
   float drop_scale;
+  // Work mapping: 0 = every XCD runs its pairs' heaviest items first; > 0 =
+  // pairs taken that many at a time (packed sequences, see prefill_work_item).
+  int32_t wi_chunk;
 };
 
 // Paged decode: query heads per kv head (one wave serves the whole group),
