@@ -408,7 +408,8 @@ int32_t fa_decode_paged_fp8_num_splits(const fa_decode_paged_fp8_args *args);
  *       starts at element p * batch * seqlen * heads * head_dim).
  *   lse_parts: DEVICE fp32 [P, batch, heads, seqlen] contiguous, natural
  *       log.  -inf marks a row for which part p saw no key: its o_p row is
- *       then not read.  Values must not be NaN or +inf.
+ *       then ignored (it may hold anything, NaN included).  Values must not
+ *       be NaN or +inf.
  *   o: DEVICE [batch, seqlen, heads, head_dim] contiguous (written); must not
  *       overlap the inputs.
  *   lse: DEVICE fp32 [batch, heads, seqlen] (written; may be NULL).
