@@ -48,8 +48,9 @@
 //   * dropout (a compile-time variant, as "FlashAttention: The Algorithm That
 //     Beat the Memory Wall", "Why Templates Matter Here", describes the
 //     kernel family): each weight is kept or zeroed by one byte of a
-//     counter-based generator drawn in registers during the softmax, so no
-//     mask is stored; the dropped weights still count in l, and O is scaled
+//     counter-based generator drawn in registers (in the MFMA phase before
+//     the tile's softmax, where the vector ALU is idle), so no mask is
+//     stored; the dropped weights still count in l, and O is scaled
 //     by 256 / (256 - t) at the end (t the byte threshold).
 //   * the first-tile NaN of "exp(-inf - -inf)" ("S12 FlashAttention", "Build
 //     it / Implementation") is avoided by substituting 0 for a -inf reference
@@ -350,6 +351,27 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
   };
 
+  // Dropout bytes of tile t into dw.  Both halves of the wave hold the same
+  // row: lane half hi draws the 16-key groups 2u + hi, and one swap across
+  // the halves hands each lane the words it needs from the other half's draw
+  // (lanes 0..31 keep words 0 and 2, lanes 32..63 words 1 and 3, of every
+  // group).  A tile's draw runs in the MFMA phase before its softmax, where
+  // the vector ALU is otherwise idle, and the softmax only applies it.
+  auto draw = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 r = philox4x32_10(
+          make_uint4((uint32_t)(4 * t + 2 * u + hi), (uint32_t)rid, (uint32_t)(rid >> 32), p.drop_offset),
+          p.drop_seed_lo, p.drop_seed_hi);
+      const auto w01 = __builtin_amdgcn_permlane32_swap(r.x, r.y, false, false);
+      const auto w23 = __builtin_amdgcn_permlane32_swap(r.z, r.w, false, false);
+      dw[2 * u][0] = w01[0];
+      dw[2 * u + 1][0] = w01[1];
+      dw[2 * u][1] = w23[0];
+      dw[2 * u + 1][1] = w23[1];
+    }
+  };
+
   auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
@@ -361,24 +383,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > kend) sacc[kb][r] = -INFINITY;
-    }
-    if (DROP) {
-      // Both halves of the wave hold the same row: lane half hi draws the
-      // 16-key groups 2u + hi, and one swap across the halves hands each
-      // lane the words it needs from the other half's draw (lanes 0..31 keep
-      // words 0 and 2, lanes 32..63 words 1 and 3, of every group).
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint4 r = philox4x32_10(
-            make_uint4((uint32_t)(4 * t + 2 * u + hi), (uint32_t)rid, (uint32_t)(rid >> 32), p.drop_offset),
-            p.drop_seed_lo, p.drop_seed_hi);
-        const auto w01 = __builtin_amdgcn_permlane32_swap(r.x, r.y, false, false);
-        const auto w23 = __builtin_amdgcn_permlane32_swap(r.z, r.w, false, false);
-        dw[2 * u][0] = w01[0];
-        dw[2 * u + 1][0] = w01[1];
-        dw[2 * u][1] = w23[0];
-        dw[2 * u + 1][1] = w23[1];
-      }
     }
     // Fast path: weights against the current reference m_run, without the
     // tile's row max.  Every weight is at most this lane's partial sum, so a
@@ -493,6 +497,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     // (both count on the same counter), and arrives during the barrier.
     if (grp == 0) {
       scores(0);
+      if (DROP) draw(0);
       int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
       for (int t = 0; t < nt; ++t) {
@@ -500,6 +505,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
+        if (DROP && t + 1 < nt) draw(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -512,12 +518,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       int32_t ph = pool_block(3 < nt ? 3 : -1);
       phase_end(0);
       scores(0);
+      if (DROP) draw(0);
       phase_end(1);
       for (int t = 0; t < nt; ++t) {
         softmax(t, t + 3 < nt ? t + 3 : -1, false, ph);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
         if (t + 1 < nt) scores(t + 1);
+        if (DROP && t + 1 < nt) draw(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
