@@ -3,7 +3,7 @@
 * seeded partial results (``inputs.merge_case``) over head dims 64/128/256,
   bf16 and fp32, 1..8 parts, ragged row counts, with and without shards
   that saw no key (lse -inf, output NaN);
-* ring attention over key shards on one GPU: each query chunk's results
+* ring attention over key shards on one GPU (bf16, and fp32 at the fp32 bound): each query chunk's results
   against the key shards before it (plain) and its own shard (causal), from
   fa_fwd, merged, against the oracle's causal attention over the whole
   sequence;
@@ -181,3 +181,23 @@ def test_merge_bench_size_sampled(gpu):
     og = o[:, torch.from_numpy(rows).cuda()]
     check_merge(host(og), lse[:, :, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64), o_ref,
                 l_ref, "bf16", "merge workload 12 sampled")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_ring_attention_fp32(gpu, d):
+    """fp32 ring over two key shards: the merged result keeps the fp32 bound."""
+    N, chunks, H = 512, 2, 2
+    case = inputs.dense_case(8400 + d, 1, N, N, H, H, d, dtype="f32")
+    q, k, v = (torch.from_numpy(case[n]).cuda() for n in ("q", "k", "v"))
+    o_ref, l_ref = oracle.dense(case["q"], case["k"], case["v"], causal=True)
+    cl = N // chunks
+    for c in range(chunks):
+        qs = slice(c * cl, (c + 1) * cl)
+        parts = [gpu.fa_fwd(q[:, qs].contiguous(), k[:, s * cl:(s + 1) * cl].contiguous(),
+                            v[:, s * cl:(s + 1) * cl].contiguous(), causal=(s == c)) for s in range(c + 1)]
+        o, lse = gpu.fa_merge_states(torch.stack([p[0] for p in parts]).contiguous(),
+                                     torch.stack([p[1] for p in parts]).contiguous())
+        torch.cuda.synchronize()
+        err = np.abs(o.cpu().numpy().astype(np.float64).transpose(0, 2, 1, 3) - o_ref[:, :, qs])
+        assert err.max() <= 1e-5, f"fp32 ring d={d} chunk {c}: {err.max():.3e}"
+        assert np.abs(lse.cpu().numpy() - l_ref[:, :, qs]).max() <= 1e-5
