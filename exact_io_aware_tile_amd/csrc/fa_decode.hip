@@ -64,7 +64,7 @@ constexpr int kBlock = 16;
 constexpr float kLazyLog2 = 8.f;    // largest weight 2^8 against a stale reference
 constexpr float kInitMax = -1e30f;  // finite initial reference max
 constexpr int kMlStride = 4;        // workspace floats per partial: m, l, lb, unused
-constexpr int kSplitWavesPerCu = 8; // occupancy the split kernel is built for
+constexpr int kSplitWavesPerCu = 12; // occupancy the split kernel is built for (bf16, head_dim 64 / 128)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
@@ -175,14 +175,15 @@ struct Blk {
   uint4 v[KV8 ? D / 64 : D / 32];
 };
 
-// Blocks in flight per wave (the register ring): four, or two at head_dim
-// 256 with bf16 pools, where a block is 16 KB per operand and the ring would
-// otherwise take every register, and two with E4M3 pools, whose waves are
-// bound by their per-block chain of waits rather than by bytes in flight:
-// the registers go to a fourth wave per SIMD instead (measured: 424 -> 393 us
-// on B=64 Hq=32 Hkv=8 d=128 lengths U{1024..32768}).
+// Blocks in flight per wave (the register ring): two.  The waves are bound
+// by their per-block chain of waits rather than by bytes in flight, so the
+// registers of a deeper ring serve better as more waves per SIMD (measured
+// on B=64 Hq=32 Hkv=8 d=128, lengths U{1024..32768}, against a four-block
+// ring: E4M3 pools 424 -> 393 us at four waves instead of three, bf16 pools
+// 698 -> 686 us at three instead of two).  At head_dim 256 with bf16 pools a
+// block is 16 KB per operand and two blocks already take most registers.
 template <int D, bool KV8>
-constexpr int ring_depth() { return (D == 256 && !KV8) || KV8 ? 2 : 4; }
+constexpr int ring_depth() { return 2; }
 
 // Two E4M3 bytes (0, 1 or, with HI, 2, 3 of w) -> two bf16, exactly (scale 1).
 template <bool HI>
@@ -195,12 +196,12 @@ __device__ __forceinline__ uint4 e4m3x8_bf16x8(uint32_t a, uint32_t b) {
                     e4m3x2_bf16x2<true>(b));
 }
 
-// Waves per SIMD the split kernel is built for: two, or one at head_dim 256
-// (its ring, accumulator and Q fragments need more than 256 registers; the
-// rest goes to the accumulation registers), or four with E4M3 pools (a
-// two-block ring; 128 registers, a few values spill).
+// Waves per SIMD the split kernel is built for: three (168 registers), or
+// one at head_dim 256 (its ring, accumulator and Q fragments need more than
+// 256 registers; the rest goes to the accumulation registers), or four with
+// E4M3 pools (128 registers).  A few values spill at three and four.
 template <int D, bool KV8 = false>
-constexpr int split_waves_per_simd() { return D == 256 ? 1 : (KV8 ? 4 : 2); }
+constexpr int split_waves_per_simd() { return D == 256 ? 1 : (KV8 ? 4 : 3); }
 
 template <int D, bool KV8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<D, KV8>(),
@@ -522,8 +523,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecodeParams p
 int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim,
                      bool kv8) {
   if (num_splits > 0) return num_splits;
-  // One part per wave slot of the device (the split kernel is built for two
-  // waves per SIMD, eight per CU; one and four at head_dim 256; four and
+  // One part per wave slot of the device (the split kernel is built for three
+  // waves per SIMD, twelve per CU; one and four at head_dim 256; four and
   // sixteen for FP8 pools below 256), spread over the kv heads; no more parts
   // than about one per 4 blocks of the largest possible batch.
   int dev = 0, cus = 0;
