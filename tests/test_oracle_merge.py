@@ -13,7 +13,7 @@ combine by rescaling to the larger max and adding.  Its pins:
   FlashAttention", "What this unlocks beyond speed", ring attention);
 * the page's worked example (printed to three decimals) and its closed form
   from the printed row;
-* the page's pairwise (m, l, o) merge (``oracle.recurrence.merge``) applied
+* the page's pairwise (m, l, o) merge (``oracle.recurrence.combine``) applied
   part after part;
 * special cases: one part is the identity, parts with lse = -inf are
   skipped whatever their output holds, rows no part saw are 0 / -inf, and a
@@ -97,10 +97,11 @@ def test_matches_pairwise_recurrence_merge():
     rng = np.random.default_rng(5)
     P, d = 5, 6
     states = [(float(rng.normal(0, 4)), float(rng.uniform(0.5, 9)), rng.standard_normal(d)) for _ in range(P)]
-    acc = states[0]
-    for st in states[1:]:
-        acc = recurrence.merge(acc, st)
-    m, l, ou = acc
+    rows = [recurrence.Rows(np.array([m_]), np.array([l_]), o_[None]) for m_, l_, o_ in states]
+    acc = rows[0]
+    for st in rows[1:]:
+        acc = recurrence.combine(acc, st)
+    m, l, ou = float(acc.mx[0]), float(acc.total[0]), acc.acc[0]
     o_parts = np.stack([(o_ / l_)[None] for _, l_, o_ in states])
     lse_parts = np.array([[m_ + np.log(l_)] for m_, l_, _ in states])
     o, lse = oracle.merge_states(o_parts, lse_parts)

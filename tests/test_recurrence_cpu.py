@@ -52,7 +52,7 @@ def test_tiled_equals_oracle(tile, n):
     d = 16
     q, k, v = rnd(n, d), rnd(n + 1, n, d), rnd(n + 2, n, d)
     o, lse = oracle.dense(q[None, None, None], k[None, :, None], v[None, :, None], causal=False)
-    of, lf = rec.flash_row(q, k, v, tile, 1.0 / math.sqrt(d))
+    of, lf = rec.stream(q, k, v, tile, 1.0 / math.sqrt(d))
     np.testing.assert_allclose(of, o[0, 0, 0], atol=TOL, rtol=0)
     assert abs(lf - lse[0, 0, 0]) < TOL
 
@@ -63,7 +63,7 @@ def test_tiled_causal_equals_oracle():
     o, lse = oracle.dense(q[None, :, None], k[None, :, None], v[None, :, None], causal=True)
     for i in range(N):
         vis = np.arange(N) <= i
-        of, lf = rec.flash_row(q[i], k, v, tile, 1.0 / math.sqrt(d), visible=vis)
+        of, lf = rec.stream(q[i], k, v, tile, 1.0 / math.sqrt(d), visible=vis)
         np.testing.assert_allclose(of, o[0, 0, i], atol=TOL, rtol=0)
         assert abs(lf - lse[0, 0, i]) < TOL
 
@@ -74,10 +74,11 @@ def test_intermediate_state_is_prefix_softmax():
     N, d, tile = 40, 8, 8
     q, k, v = rnd(53, d), rnd(54, N, d), rnd(55, N, d)
     scale = 1.0 / math.sqrt(d)
-    st = rec.init_state(d)
+    st = rec.empty(1, d)
     for start in range(0, N, tile):
-        st = rec.update(st, (k[start:start + tile] @ q) * scale, v[start:start + tile])
-        o_part, l_part = rec.finish(st)
+        st = rec.absorb(st, ((k[start:start + tile] @ q) * scale)[None], v[start:start + tile])
+        o_part, l_part = rec.readout(st)
+        o_part, l_part = o_part[0], l_part[0]
         seen = start + tile
         o, lse = oracle.dense(q[None, None, None], k[None, :seen, None], v[None, :seen, None],
                               causal=False)
@@ -96,7 +97,7 @@ def test_paged_equals_oracle(seq_len):
     t = np.arange(seq_len)
     kk, vv = k_cache[table[t // bs], t % bs], v_cache[table[t // bs], t % bs]
     o, lse = oracle.dense(q[None, None, None], kk[None, :, None], vv[None, :, None], causal=False)
-    op, lp = rec.paged_row(q, table, k_cache, v_cache, seq_len, bs, 1.0 / math.sqrt(d))
+    op, lp = rec.paged(q, table, k_cache, v_cache, seq_len, bs, 1.0 / math.sqrt(d))
     np.testing.assert_allclose(op, o[0, 0, 0], atol=TOL, rtol=0)
     assert abs(lp - lse[0, 0, 0]) < TOL
 
@@ -106,7 +107,7 @@ def test_split_four_workers_equals_oracle(n):
     d = 16
     q, k, v = rnd(60, d), rnd(61, n, d), rnd(62, n, d)
     o, lse = oracle.dense(q[None, None, None], k[None, :, None], v[None, :, None], causal=False)
-    os_, ls = rec.split_row(q, k, v, workers=4, tile=16, scale=1.0 / math.sqrt(d))
+    os_, ls = rec.split(q, k, v, workers=4, tile=16, scale=1.0 / math.sqrt(d))
     np.testing.assert_allclose(os_, o[0, 0, 0], atol=TOL, rtol=0)
     assert abs(ls - lse[0, 0, 0]) < TOL
 
@@ -116,9 +117,9 @@ def test_fully_masked_first_tile_nan_and_guard():
     q, k, v = rnd(63, d), rnd(64, N, d), rnd(65, N, d)
     vis = np.arange(N) >= tile  # the whole first tile is masked
     with np.errstate(invalid="ignore"):
-        o_bad, _ = rec.flash_row(q, k, v, tile, 0.5, visible=vis, guard=False)
+        o_bad, _ = rec.stream(q, k, v, tile, 0.5, visible=vis, guard=False)
     assert np.isnan(o_bad).all()
-    o_ok, l_ok = rec.flash_row(q, k, v, tile, 0.5, visible=vis, guard=True)
+    o_ok, l_ok = rec.stream(q, k, v, tile, 0.5, visible=vis, guard=True)
     o, lse = oracle.dense(q[None, None, None], k[None, tile:, None], v[None, tile:, None],
                           causal=False, scale=0.5)
     np.testing.assert_allclose(o_ok, o[0, 0, 0], atol=TOL, rtol=0)
@@ -127,8 +128,17 @@ def test_fully_masked_first_tile_nan_and_guard():
 
 def test_merge_with_empty_state_is_identity():
     d = 4
-    st = rec.update(rec.init_state(d), np.array([0.3, -1.0]), rnd(66, 2, d))
-    m = rec.merge(st, rec.init_state(d))
-    assert m[0] == st[0] and m[1] == st[1] and np.array_equal(m[2], st[2])
-    m2 = rec.merge(rec.init_state(d), st)
-    assert m2[0] == st[0] and m2[1] == st[1] and np.array_equal(m2[2], st[2])
+    st = rec.absorb(rec.empty(1, d), np.array([[0.3, -1.0]]), rnd(66, 2, d))
+    for m in (rec.combine(st, rec.empty(1, d)), rec.combine(rec.empty(1, d), st)):
+        assert m.mx[0] == st.mx[0] and m.total[0] == st.total[0] and np.array_equal(m.acc, st.acc)
+
+
+def test_many_rows_at_once_equal_one_row_at_a_time():
+    N, d = 45, 8
+    q, k, v = rnd(67, 6, d), rnd(68, N, d), rnd(69, N, d)
+    vis = np.arange(N)[None, :] <= (np.arange(6)[:, None] * 7 + 3)
+    o, lse = rec.stream(q, k, v, 16, 0.4, visible=vis)
+    for i in range(6):
+        oi, li = rec.stream(q[i], k, v, 16, 0.4, visible=vis[i])
+        np.testing.assert_allclose(o[i], oi, atol=1e-15, rtol=0)
+        assert abs(lse[i] - li) < 1e-15
