@@ -124,6 +124,13 @@ def lib(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    _lib = load(path)
+    return _lib
+
+
+def load(path: str):
+    """Load a build of the library from ``path`` with the argument types set
+    (``lib()`` caches the product; tests load other builds with this)."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run `python -m exact_io_aware_tile_amd.build`")
     L = ctypes.CDLL(path)
@@ -163,7 +170,6 @@ def lib(path: str = LIB_PATH):
     L.fa_last_error.restype = ctypes.c_char_p
     L.fa_abi_version.argtypes = []
     L.fa_abi_version.restype = _I32
-    _lib = L
     return L
 
 
@@ -194,9 +200,38 @@ def _dev(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("tensors must be on the GPU")
+    _same_device(*ts)
     for t in ts:
         if t is not None and t.dim() > 0 and t.stride(-1) != 1:
             raise ValueError("the last dimension must be contiguous")
+
+
+def _need(t, name, shape=None, dtype=None, contiguous=False, optional=False):
+    """Reject a tensor whose shape, dtype or layout disagrees with the call:
+    the library trusts the sizes it is given, so a short output or a
+    mismatched operand would be read or written out of bounds."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ndim(t, name, n):
+    if t is None or t.dim() != n:
+        raise ValueError(f"{name} must be a {n}-D tensor")
+
+
+def _same_device(*ts):
+    ref = next(t for t in ts if t is not None)
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"all tensors must be on {ref.device}, got one on {t.device}")
 
 
 def _stream(stream):
@@ -234,8 +269,25 @@ def fa_fwd_dropout(q, k, v, *, dropout_p: float, seed: int, offset: int = 0, cau
     return out, lse
 
 
+def _check_dense(q, k, v, out, lse, qdt, odt):
+    """Shapes and dtypes of a dense call: q [B, Nq, Hq, d], k and v
+    [B, Nk, Hkv, d], out [B, Nq, Hq, d], lse [B, Hq, Nq] fp32 contiguous."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _ndim(t, n, 4)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    _need(q, "q", dtype=qdt)
+    _need(k, "k", (B, Nk, Hkv, d), qdt)
+    _need(v, "v", (B, Nk, Hkv, d), qdt)
+    _need(out, "out", (B, Nq, Hq, d), odt, optional=True)
+    _need(lse, "lse", (B, Hq, Nq), torch.float32, contiguous=True, optional=True)
+
+
 def _fwd_args(q, k, v, causal, scale, out, lse, return_lse):
     torch = _torch()
+    _dtype_code(q)
+    _check_dense(q, k, v, out, lse, q.dtype, q.dtype)
     _dev(q, k, v, out, lse)
     B, Nq, Hq, d = q.shape
     _, Nk, Hkv, _ = k.shape
@@ -260,10 +312,11 @@ def fa_fwd_fp8(q, k, v, descale, *, causal: bool = False, scale: float | None = 
     [B, Nk, Hkv, d]) standing for descale[i] * value(code).  Returns (o, lse)
     with o in bf16."""
     torch = _torch()
-    _dev(q, k, v, out, lse)
     for t in (q, k, v):
-        if t.dtype != torch.uint8:
+        if t is not None and t.dtype != torch.uint8:
             raise TypeError("fa_fwd_fp8 takes E4M3 codes as uint8 tensors")
+    _check_dense(q, k, v, out, lse, torch.uint8, torch.bfloat16)
+    _dev(q, k, v, out, lse)
     B, Nq, Hq, d = q.shape
     _, Nk, Hkv, _ = k.shape
     if out is None:
@@ -301,11 +354,30 @@ def fa_fwd_varlen_dropout(q, k, v, cu_seqlens, max_seqlen: int, *, dropout_p: fl
     return out, lse
 
 
+def _check_varlen(q, k, v, cu_seqlens, out, lse, qdt, odt):
+    """Shapes and dtypes of a packed call: q [T, Hq, d], k and v [T, Hkv, d],
+    cu_seqlens int32 [S + 1] contiguous, out [T, Hq, d], lse [Hq, T] fp32."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _ndim(t, n, 3)
+    _ndim(cu_seqlens, "cu_seqlens", 1)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", dtype=qdt)
+    _need(k, "k", (T, Hkv, d), qdt)
+    _need(v, "v", (T, Hkv, d), qdt)
+    _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, contiguous=True)
+    if cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens needs at least one entry")
+    _need(out, "out", (T, Hq, d), odt, optional=True)
+    _need(lse, "lse", (Hq, T), torch.float32, contiguous=True, optional=True)
+
+
 def _varlen_args(q, k, v, cu_seqlens, max_seqlen, causal, scale, out, lse, return_lse):
     torch = _torch()
+    _dtype_code(q)
+    _check_varlen(q, k, v, cu_seqlens, out, lse, q.dtype, q.dtype)
     _dev(q, k, v, out, lse, cu_seqlens)
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     if out is None:
@@ -330,12 +402,11 @@ def fa_fwd_varlen_fp8(q, k, v, cu_seqlens, max_seqlen: int, descale, *, causal: 
     """Packed attention over FP8 E4M3 codes (uint8 q [T, Hq, d], k/v [T, Hkv, d])
     standing for descale[i] * value(code).  Returns (o, lse), o in bf16."""
     torch = _torch()
-    _dev(q, k, v, out, lse, cu_seqlens)
     for t in (q, k, v):
-        if t.dtype != torch.uint8:
+        if t is not None and t.dtype != torch.uint8:
             raise TypeError("fa_fwd_varlen_fp8 takes E4M3 codes as uint8 tensors")
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
+    _check_varlen(q, k, v, cu_seqlens, out, lse, torch.uint8, torch.bfloat16)
+    _dev(q, k, v, out, lse, cu_seqlens)
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     if out is None:
@@ -354,6 +425,37 @@ def fa_fwd_varlen_fp8(q, k, v, cu_seqlens, max_seqlen: int, descale, *, causal: 
     a.causal = int(bool(causal))
     _check(lib().fa_fwd_varlen_fp8(ctypes.byref(a), _stream(stream)))
     return out, lse
+
+
+def _check_pools(k_pool, v_pool, d, dt):
+    """Pools [num_blocks, heads_kv, block_size, d] (any strides with d
+    contiguous), k and v alike."""
+    _ndim(k_pool, "k_pool", 4)
+    _ndim(v_pool, "v_pool", 4)
+    if k_pool.shape[3] != d:
+        raise ValueError(f"pools must have head_dim {d}, got {k_pool.shape[3]}")
+    _need(k_pool, "k_pool", dtype=dt)
+    _need(v_pool, "v_pool", tuple(k_pool.shape), dt)
+    if tuple(k_pool.stride()) != tuple(v_pool.stride()):
+        raise ValueError("k_pool and v_pool must share shape and strides")
+
+
+def _check_paged_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse, qdt, odt):
+    torch = _torch()
+    _ndim(q, "q", 3)
+    Tq, Hq, d = q.shape
+    _need(q, "q", dtype=qdt)
+    _check_pools(k_pool, v_pool, d, qdt)
+    _ndim(cu_seqlens_q, "cu_seqlens_q", 1)
+    _need(cu_seqlens_q, "cu_seqlens_q", dtype=torch.int32, contiguous=True)
+    S = cu_seqlens_q.numel() - 1
+    if S < 0:
+        raise ValueError("cu_seqlens_q needs at least one entry")
+    _ndim(block_table, "block_table", 2)
+    _need(block_table, "block_table", (S, block_table.shape[1]), torch.int32, contiguous=True)
+    _need(seq_lens_k, "seq_lens_k", (S,), torch.int32, contiguous=True)
+    _need(out, "out", (Tq, Hq, d), odt, optional=True)
+    _need(lse, "lse", (Hq, Tq), torch.float32, contiguous=True, optional=True)
 
 
 def _fwd_paged_args(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q, max_seqlen_k,
@@ -383,14 +485,12 @@ def fa_fwd_paged(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_s
     """Chunked prefill over a paged KV pool (bf16).  ``max_seqlen_q`` and
     ``max_seqlen_k`` are host-side bounds.  Returns (o, lse)."""
     torch = _torch()
+    for t in (q, k_pool, v_pool):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise TypeError("fa_fwd_paged takes bf16 q and pools")
+    _check_paged_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse, torch.bfloat16,
+                         torch.bfloat16)
     _dev(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse)
-    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q), ("seq_lens_k", seq_lens_k)):
-        if t.dtype != torch.int32:
-            raise TypeError(f"{name} must be int32")
-    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
-        raise TypeError("fa_fwd_paged takes bf16 q and pools")
-    if not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
     Tq, Hq, _ = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -402,6 +502,23 @@ def fa_fwd_paged(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, max_s
     a.o_stride[:] = list(out.stride()[:2])
     _check(lib().fa_fwd_paged(ctypes.byref(a), _stream(stream)))
     return out, lse
+
+
+def _check_decode(q, k_pool, v_pool, block_table, seq_lens, out, lse, workspace, pool_dt):
+    """q [B, Hq, d] bf16, pools [blocks, Hkv, 16, d] of pool_dt, block_table
+    int32 [B, max_blocks] contiguous, seq_lens int32 [B], out [B, Hq, d] bf16,
+    lse [B, Hq] fp32 contiguous, workspace contiguous."""
+    torch = _torch()
+    _ndim(q, "q", 3)
+    B, Hq, d = q.shape
+    _need(q, "q", dtype=torch.bfloat16)
+    _check_pools(k_pool, v_pool, d, pool_dt)
+    _ndim(block_table, "block_table", 2)
+    _need(block_table, "block_table", (B, block_table.shape[1]), torch.int32, contiguous=True)
+    _need(seq_lens, "seq_lens", (B,), torch.int32, contiguous=True)
+    _need(out, "out", (B, Hq, d), torch.bfloat16, optional=True)
+    _need(lse, "lse", (B, Hq), torch.float32, contiguous=True, optional=True)
+    _need(workspace, "workspace", contiguous=True, optional=True)
 
 
 def _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, num_splits):
@@ -425,12 +542,14 @@ def _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, n
 
 def fa_decode_paged_workspace_size(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, *,
                                    num_splits: int = 0) -> int:
+    _check_decode(q, k_pool, v_pool, block_table, seq_lens, None, None, None, _torch().bfloat16)
     a = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, None, num_splits)
     return int(lib().fa_decode_paged_workspace_size(ctypes.byref(a)))
 
 
 def fa_decode_paged_num_splits(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, *,
                                num_splits: int = 0) -> int:
+    _check_decode(q, k_pool, v_pool, block_table, seq_lens, None, None, None, _torch().bfloat16)
     a = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, None, num_splits)
     return int(lib().fa_decode_paged_num_splits(ctypes.byref(a)))
 
@@ -440,11 +559,8 @@ def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, 
                     return_lse: bool = True, workspace=None, stream=None):
     """Paged single-token decode.  Returns (o, lse)."""
     torch = _torch()
-    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse)
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise TypeError("block_table and seq_lens must be int32")
-    if not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
+    _check_decode(q, k_pool, v_pool, block_table, seq_lens, out, lse, workspace, torch.bfloat16)
+    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse, workspace)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -468,13 +584,11 @@ def fa_decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: i
     standing for descale[0] * value(k code) and descale[1] * value(v code);
     q and o bf16.  Returns (o, lse)."""
     torch = _torch()
-    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse)
-    if k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
-        raise TypeError("fa_decode_paged_fp8 takes E4M3 pools as uint8 tensors")
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise TypeError("block_table and seq_lens must be int32")
-    if not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
+    for t in (k_pool, v_pool):
+        if t is not None and t.dtype != torch.uint8:
+            raise TypeError("fa_decode_paged_fp8 takes E4M3 pools as uint8 tensors")
+    _check_decode(q, k_pool, v_pool, block_table, seq_lens, out, lse, workspace, torch.uint8)
+    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse, workspace)
     B, Hq, d = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -494,6 +608,7 @@ def fa_decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: i
 
 
 def _decode_fp8_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, descale, num_splits):
+    _check_decode(q, k_pool, v_pool, block_table, seq_lens, None, None, None, _torch().uint8)
     a = DecodePagedFp8Args()
     a.base = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, None, num_splits)
     a.k_descale, a.v_descale = (float(x) for x in descale)
@@ -518,14 +633,12 @@ def fa_fwd_paged_fp8(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, m
     """Chunked prefill over an FP8 KV cache: uint8 E4M3 q [Tq, Hq, d] and pools
     standing for descale[i] * value(code) (q, k, v).  Returns (o, lse), o bf16."""
     torch = _torch()
+    for t in (q, k_pool, v_pool):
+        if t is not None and t.dtype != torch.uint8:
+            raise TypeError("fa_fwd_paged_fp8 takes E4M3 q and pools as uint8 tensors")
+    _check_paged_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse, torch.uint8,
+                         torch.bfloat16)
     _dev(q, k_pool, v_pool, block_table, cu_seqlens_q, seq_lens_k, out, lse)
-    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q), ("seq_lens_k", seq_lens_k)):
-        if t.dtype != torch.int32:
-            raise TypeError(f"{name} must be int32")
-    if q.dtype != torch.uint8 or k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
-        raise TypeError("fa_fwd_paged_fp8 takes E4M3 q and pools as uint8 tensors")
-    if not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous (row stride max_blocks_per_seq)")
     Tq, Hq, d = q.shape
     if out is None:
         out = torch.empty((Tq, Hq, d), dtype=torch.bfloat16, device=q.device)
@@ -545,7 +658,6 @@ def fa_merge_states(o_parts, lse_parts, *, out=None, lse=None, return_lse: bool 
     """Merge P results over disjoint key sets: o_parts [P, B, S, H, D] and
     lse_parts [P, B, H, S] (contiguous) -> (o [B, S, H, D], lse [B, H, S])."""
     torch = _torch()
-    _dev(o_parts, lse_parts, out, lse)
     if o_parts.dim() != 5 or lse_parts.dim() != 4:
         raise ValueError("o_parts must be [P, B, S, H, D] and lse_parts [P, B, H, S]")
     P, B, S, H, D = o_parts.shape
@@ -553,6 +665,9 @@ def fa_merge_states(o_parts, lse_parts, *, out=None, lse=None, return_lse: bool 
         raise ValueError(f"lse_parts must be fp32 {(P, B, H, S)}, got {tuple(lse_parts.shape)} {lse_parts.dtype}")
     if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
         raise ValueError("o_parts and lse_parts must be contiguous")
+    _need(out, "out", (B, S, H, D), o_parts.dtype, contiguous=True, optional=True)
+    _need(lse, "lse", (B, H, S), torch.float32, contiguous=True, optional=True)
+    _dev(o_parts, lse_parts, out, lse)
     if out is None:
         out = torch.empty((B, S, H, D), dtype=o_parts.dtype, device=o_parts.device)
     if lse is None and return_lse:
