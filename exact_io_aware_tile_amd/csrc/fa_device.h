@@ -75,11 +75,28 @@ __device__ __forceinline__ void dma_16b(const void* base, uint32_t off, uint32_t
       : "memory");
 }
 
+// Race check.  The prefill pipelines order their LDS ring by hand: each wave
+// waits for exactly the DMA loads the next phase reads (wait_vmcnt<N>) and
+// then meets the others at a fence-free barrier (lds_barrier).  Built with
+// FA_SYNC_CHECK defined (a separate checking library, never the product),
+// every such wait drains all of the wave's memory operations and every
+// barrier is a full __syncthreads; a correct hand ordering gives the same
+// bits, so any difference between the two builds exposes a stage read
+// before its data landed or overwritten while still being read.
+#ifdef FA_SYNC_CHECK
+constexpr bool kSyncCheck = true;
+#else
+constexpr bool kSyncCheck = false;
+#endif
+
 // s_waitcnt immediates (gfx9 encoding): vmcnt(N) with expcnt / lgkmcnt left open.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  if (kSyncCheck)
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
 // Workgroup barrier for the LDS ring.  __syncthreads() carries a release
@@ -93,7 +110,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (MFMA and exponentials included) inside the phase.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
+  if (kSyncCheck) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  } else {
+    asm volatile("s_barrier" ::: "memory");
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
