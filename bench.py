@@ -20,7 +20,9 @@ KV cache and the merge of 8 key-shard results of the long-context shape
 One JSON line is printed.  "roofline" is the prefill kernel's algorithmic
 TFLOP/s (4*d flops per visible query/key pair) against the 2.5 PFLOP/s dense
 bf16 MFMA peak; "cpu_baseline" is the fp64 oracle timed on this host's cores
-on a bounded sample of the same workload's rows.
+on a bounded sample of the same workload's rows, and "parity" compares the
+outputs the timed steps left behind with the oracle on sampled rows (the
+oracle runs only in that final leg, after all GPU timing).
 """
 from __future__ import annotations
 
@@ -31,6 +33,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -40,6 +44,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
+    "long": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "decode": ["exact_io_aware_tile_amd/csrc/fa_decode.hip"],
     "chunked": ["exact_io_aware_tile_amd/csrc/fa_fwd_bf16.hip"],
     "fp8": ["exact_io_aware_tile_amd/csrc/fa_fwd_fp8.hip"],
@@ -95,6 +100,23 @@ def measured_traffic(kind: str):
 
 def bf16_dev(a, torch, np):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+INPUT_KEYS = ("q", "k", "v", "k_pool", "v_pool", "block_table", "seq_lens", "cu_seqlens", "cu_seqlens_q",
+              "o_parts", "lse_parts")
+
+
+def input_digest(case) -> str:
+    """sha256 of the host bytes of every input array of a workload (the bytes
+    copied to the device), in INPUT_KEYS order."""
+    import numpy as np
+    h = hashlib.sha256()
+    for key in INPUT_KEYS:
+        a = case.get(key)
+        if isinstance(a, np.ndarray):
+            h.update(key.encode())
+            h.update(np.ascontiguousarray(a).view(np.uint8).reshape(-1).data)
+    return h.hexdigest()
 
 
 SETTLE_S = 0.3  # untimed seconds of the same step before the warm-up steps
@@ -174,28 +196,105 @@ def prefill_flops(case) -> float:
     return 4.0 * d * pairs * B * H
 
 
-def cpu_baseline(case, seconds, np):
+def edge_rows(rng, heads, n, extra):
+    """Row ids h*n + i (of one sequence of n rows over `heads` heads): random
+    rows plus rows at the edges of 64- and 256-row tiles and the last rows."""
+    ids = set(rng.integers(0, heads * n, size=extra).tolist())
+    for i in (0, 1, 63, 64, 255, 256, n - 257, n - 256, n - 65, n - 64, n - 2, n - 1):
+        if 0 <= i < n:
+            ids.add(int(rng.integers(0, heads)) * n + i)
+    return np.array(sorted(ids), dtype=np.int64)
+
+
+def parity_stats(o_gpu, lse_gpu, o_ref, lse_ref, max_tol=2e-2, mean_tol=2e-3, lse_tol=1e-3):
+    err = np.abs(o_gpu - o_ref)
+    fin = np.isfinite(lse_ref)
+    lerr = np.abs(lse_gpu[fin] - lse_ref[fin])
+    finite_ok = bool(np.isfinite(o_gpu).all() and (np.isfinite(lse_gpu) == fin).all())
+    st = {"rows": int(o_gpu.shape[0]), "max_abs_do": float(err.max()), "mean_abs_do": float(err.mean()),
+          "max_abs_dlse": float(lerr.max()) if lerr.size else 0.0}
+    st["within_contract"] = bool(finite_ok and st["max_abs_do"] <= max_tol and st["mean_abs_do"] <= mean_tol
+                                 and st["max_abs_dlse"] <= lse_tol)
+    return st
+
+
+def oracle_leg(legs, seconds):
+    """The only part of the bench that runs the fp64 oracle (test
+    infrastructure, never on the measured path), after all GPU timing:
+
+    * cpu_baseline: the oracle, untuned, timed on this host's cores on random
+      query rows of the headline workload for about `seconds`;
+    * parity: the outputs the timed GPU steps left in their buffers, compared
+      with the oracle on sampled rows (the baseline's own rows for the
+      headline, plus tile edges; a bounded sample for the other legs)."""
     import oracle
     threads = oracle.threads(0)
     try:
         threads = oracle.threads(len(os.sched_getaffinity(0)))
     except AttributeError:
         pass
-    B, N, H, d = case["batch"], case["nq"], case["hq"], case["d"]
-    rng = np.random.default_rng(1234)
-    flops = 0.0
-    rows_done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        rows = rng.integers(0, B * H * N, size=256)
-        oracle.dense(case["q"], case["k"], case["v"], causal=True, rows=rows, nthreads=threads)
-        i = rows % N
-        flops += float(4.0 * d * (i + 1).sum())
-        rows_done += rows.size
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} query rows drawn uniformly from the workload's {B * H * N} "
-                      f"(b, h, i) rows, fp64 materialised-score oracle, {el:.1f} s wall"}
+    parity = {}
+    base = None
+    for key, (case, res) in legs.items():
+        outs = res.get("outputs")
+        if outs is None:
+            continue
+        og, lg = outs
+        rng = np.random.default_rng(1234)
+        if key == "prefill":
+            B, N, H, d = case["batch"], case["nq"], case["hq"], case["d"]
+            o_rows = og.reshape(B, N, H, d).transpose(0, 2, 1, 3).reshape(B * H * N, d)
+            l_rows = lg.reshape(-1)
+            flops, done, errs = 0.0, [], []
+            t0 = time.perf_counter()
+            first = True
+            while first or time.perf_counter() - t0 < seconds:
+                rows = rng.integers(0, B * H * N, size=256)
+                if first:  # tile edges of a random (b, h)
+                    bh = int(rng.integers(0, B * H))
+                    rows = np.concatenate([rows, bh * N + edge_rows(rng, 1, N, 0)])
+                first = False
+                o_ref, l_ref = oracle.dense(case["q"], case["k"], case["v"], causal=True, rows=rows,
+                                            nthreads=threads)
+                flops += float(4.0 * d * (rows % N + 1).sum())
+                done.append(rows)
+                errs.append((o_rows[rows], l_rows[rows], o_ref, l_ref))
+            el = time.perf_counter() - t0
+            n_rows = int(sum(r.size for r in done))
+            base = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                    "sample": f"{n_rows} query rows drawn uniformly from the workload's {B * H * N} "
+                              f"(b, h, i) rows, fp64 materialised-score oracle, {el:.1f} s wall"}
+            parity[key] = parity_stats(*(np.concatenate([e[i] for e in errs]) for i in range(4)))
+        elif key == "long":
+            B, N, H, d = case["batch"], case["nq"], case["hq"], case["d"]
+            rows = edge_rows(rng, B * H, N, 192)
+            o_rows = og.reshape(B, N, H, d).transpose(0, 2, 1, 3).reshape(B * H * N, d)
+            o_ref, l_ref = oracle.dense(case["q"], case["k"], case["v"], causal=True, rows=rows, nthreads=threads)
+            parity[key] = parity_stats(o_rows[rows], lg.reshape(-1)[rows], o_ref, l_ref)
+        elif key == "varlen":
+            T, H, d = case["total"], case["hq"], case["d"]
+            rows = set(rng.integers(0, H * T, size=256).tolist())
+            cu = case["cu_seqlens"]
+            for sq in range(len(cu) - 1):
+                for t in (cu[sq], cu[sq + 1] - 1):
+                    rows.add(int(rng.integers(0, H)) * T + int(t))
+            rows = np.array(sorted(rows), dtype=np.int64)
+            o_rows = og.reshape(T, H, d).transpose(1, 0, 2).reshape(H * T, d)
+            o_ref, l_ref = oracle.varlen(case["q"], case["k"], case["v"], cu, causal=True, rows=rows,
+                                         nthreads=threads)
+            parity[key] = parity_stats(o_rows[rows], lg.reshape(-1)[rows], o_ref, l_ref)
+        elif key == "decode":
+            B, H, d = case["q"].shape
+            rows = np.array(sorted(set(rng.integers(0, B * H, size=128).tolist())), dtype=np.int64)
+            o_ref, l_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                               case["seq_lens"], rows=rows, nthreads=threads)
+            parity[key] = parity_stats(og.reshape(B * H, d)[rows], lg.reshape(-1)[rows], o_ref, l_ref)
+    return base, parity
+
+
+def host_outputs(o, lse):
+    """The timed steps' output buffers, copied to the host as float64."""
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
 def run_prefill(fa, case, steps, warmup, torch, np, kind, flush=None):
@@ -212,6 +311,7 @@ def run_prefill(fa, case, steps, warmup, torch, np, kind, flush=None):
             fa.fa_fwd(q, k, v, causal=case["causal"], out=o, lse=lse)
 
     ms, wall_ms = time_steps(step, steps, warmup, torch)
+    outputs = host_outputs(o, lse) if kind in ("prefill", "long") else None
     flops = prefill_flops(case)
     tf = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(kind)
@@ -219,9 +319,10 @@ def run_prefill(fa, case, steps, warmup, torch, np, kind, flush=None):
     if flush is not None:
         mn, med = time_cold(step, 20, torch, flush)
         cold = {"min_us": round(mn * 1e3, 1), "median_us": round(med * 1e3, 1),
+                "tflops_at_min": round(flops / (mn * 1e-3) / 1e12, 2),
                 "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2)}
     return {
-        "ms": ms, "wall_ms": wall_ms, "tflops": tf, "flops": flops, "cold": cold,
+        "ms": ms, "wall_ms": wall_ms, "tflops": tf, "flops": flops, "cold": cold, "outputs": outputs,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
@@ -240,7 +341,7 @@ def run_varlen(fa, case, steps, warmup, torch, np):
     lens = case["lengths"].astype(np.float64)
     flops = float(4.0 * case["d"] * case["hq"] * (lens * (lens + 1) / 2).sum())
     tf = flops / (ms * 1e-3) / 1e12
-    return {"ms": ms, "tflops": tf, "flops": flops,
+    return {"ms": ms, "tflops": tf, "flops": flops, "outputs": host_outputs(o, lse),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic("varlen")}}
@@ -317,6 +418,7 @@ def run_decode(fa, case, steps, warmup, torch, np, flush=None, kind="decode"):
             fa.fa_decode_paged(q, kp, vp, bt, sl, maxlen, out=o, lse=lse, workspace=ws)
 
     ms, wall_ms = time_steps(step, steps, warmup, torch)
+    outputs = host_outputs(o, lse) if kind == "decode" else None
     L = case["seq_lens"].astype(np.int64)
     hkv, d, bs = case["hkv"], case["d"], case["block_size"]
     kv_bytes = float(2 * hkv * d * (1 if kv8 else 2) * L.sum())
@@ -330,6 +432,7 @@ def run_decode(fa, case, steps, warmup, torch, np, flush=None, kind="decode"):
         cold = {"min_us": round(mn * 1e3, 1), "median_us": round(med * 1e3, 1),
                 "gbs_at_median": round(nbytes / (med * 1e-3) / 1e9, 1)}
     return {"ms": ms, "gbs": gbs, "bytes": nbytes, "kv_bytes": kv_bytes, "num_splits": splits, "cold": cold,
+            "outputs": outputs,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}}
 
@@ -399,7 +502,7 @@ def main():
     if want("long", not args.no_extra):
         case = inputs.workload(3)
         out["long"] = (case, run_prefill(fa, case, max(5, args.steps // 5), max(2, args.warmup // 5), torch, np,
-                                         "prefill"))
+                                         "long", flush))
     if want("varlen", not args.no_extra):
         case = inputs.workload(4)
         out["varlen"] = (case, run_varlen(fa, case, max(5, args.steps // 2), max(2, args.warmup // 2), torch, np))
@@ -434,7 +537,8 @@ def main():
 
     if only:
         for k, (case, res) in out.items():
-            print(json.dumps({"workload": case["name"], **{a: b for a, b in res.items() if a != "roofline"},
+            print(json.dumps({"workload": case["name"],
+                              **{a: b for a, b in res.items() if a not in ("roofline", "outputs")},
                               "roofline": res["roofline"]}))
         return
 
@@ -457,32 +561,48 @@ def main():
                    "algorithmic_gflop_per_step": round(res["flops"] / 1e9, 3)},
         "roofline": res["roofline"],
         "kernel_ms": round(res["ms"], 4),
+        "basis": "warm: K back-to-back launches on one stream, inputs resident in HBM (201 MB of q/k/v, "
+                 "which the 256 MB last-level cache can hold); 'cold' times single launches after a 512 MB "
+                 "device write evicted that cache",
         "cold": res["cold"],
+        "inputs": {"seed": 2, "sha256": input_digest(case),
+                   "recipe": "numpy default_rng([seed, stream, chunk]) N(0,1) float32, RNE to bf16"},
     }
     if "decode" in out:
         dcase, dres = out["decode"]
         line["decode"] = {"workload": dcase["name"], "value": round(dres["gbs"], 1), "unit": "GB/s",
                           "ms_per_step": round(dres["ms"], 4), "algorithmic_bytes": dres["bytes"],
-                          "num_splits": dres["num_splits"], "roofline": dres["roofline"], "cold": dres["cold"]}
+                          "num_splits": dres["num_splits"], "roofline": dres["roofline"], "cold": dres["cold"],
+                          "inputs": {"seed": 5, "sha256": input_digest(dcase)}}
         del flush
         flush = None
         line["decode"]["copy_gbs"] = round(copy_bandwidth(torch), 1)
     extra = []
+    seeds = {"long": 3, "varlen": 4, "chunked": 6, "fp8": 7, "dropout": 8, "d256": 9, "decode_d256": 10,
+             "decode_fp8": 11, "merge": 12}
     for key in ("long", "varlen", "chunked", "fp8", "dropout", "d256", "decode_d256", "decode_fp8", "merge"):
         if key in out:
             c, r = out[key]
             if "gbs" in r:
-                extra.append({"workload": c["name"], "value": round(r["gbs"], 1), "unit": "GB/s",
-                              "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]})
+                e = {"workload": c["name"], "value": round(r["gbs"], 1), "unit": "GB/s",
+                     "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]}
             else:
-                extra.append({"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",
-                              "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]})
+                e = {"workload": c["name"], "value": round(r["tflops"], 2), "unit": "TFLOP/s",
+                     "ms_per_step": round(r["ms"], 4), "roofline": r["roofline"]}
+            if r.get("cold"):
+                e["cold"] = r["cold"]
+            e["inputs"] = {"seed": seeds[key], "sha256": input_digest(c)}
+            extra.append(e)
     if extra:
         line["extra"] = extra
     line["context"] = ("pages' figures (other hardware): 2-4x wall-clock over standard attention; "
                        "FlashAttention-1 25-40% and FlashAttention-2 50-73% of A100 peak")
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, np)
+        base, parity = oracle_leg(out, args.cpu_seconds)
+        line["cpu_baseline"] = base
+        line["parity"] = {"what": "the timed steps' outputs against the fp64 oracle on sampled rows "
+                                  "(contract: max |dO| <= 2e-2, mean |dO| <= 2e-3, max |dLSE| <= 1e-3)",
+                          **parity}
     print(json.dumps(line))
 
 
