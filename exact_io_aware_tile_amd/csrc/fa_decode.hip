@@ -42,7 +42,7 @@
 //     ds_read_b64_tr_b16 (four tokens of one dim per lane); the 16-byte
 //     chunks of each row are XOR-swizzled so the transposed reads of a
 //     half-wave hit distinct banks;
-//   * K and V of three blocks are in flight (a four-deep register ring)
+//   * K and V of the next block are in flight (a two-block register ring)
 //     while one is consumed; the pool is read with non-temporal loads.
 // Lazy correction: weights are formed against the head's current reference
 // max until one would exceed 2^8; only then is the reference moved (the max
@@ -175,15 +175,13 @@ struct Blk {
   uint4 v[KV8 ? D / 64 : D / 32];
 };
 
-// Blocks in flight per wave (the register ring): two.  The waves are bound
-// by their per-block chain of waits rather than by bytes in flight, so the
-// registers of a deeper ring serve better as more waves per SIMD (measured
-// on B=64 Hq=32 Hkv=8 d=128, lengths U{1024..32768}, against a four-block
-// ring: E4M3 pools 424 -> 393 us at four waves instead of three, bf16 pools
+// Blocks in flight per wave: a ring of two.  The waves are bound by their
+// per-block chain of waits rather than by bytes in flight, so registers
+// serve better as more waves per SIMD than as a deeper ring (measured on
+// B=64 Hq=32 Hkv=8 d=128, lengths U{1024..32768}, against a four-block ring:
+// E4M3 pools 424 -> 393 us at four waves instead of three, bf16 pools
 // 698 -> 686 us at three instead of two).  At head_dim 256 with bf16 pools a
 // block is 16 KB per operand and two blocks already take most registers.
-template <int D, bool KV8>
-constexpr int ring_depth() { return 2; }
 
 // Two E4M3 bytes (0, 1 or, with HI, 2, 3 of w) -> two bf16, exactly (scale 1).
 template <bool HI>
@@ -401,18 +399,14 @@ decode_split_kernel(const DecodeParams p) {
     }
   };
 
-  // The scheduling barriers keep each ring refill where it is written, three
-  // blocks ahead of its use, instead of letting the scheduler sink the loads
+  // The scheduling barriers keep each ring refill where it is written, one
+  // block ahead of its use, instead of letting the scheduler sink the loads
   // next to their consumers.
-  Blk<D, KV8> R0, R1, R2, R3;
+  Blk<D, KV8> R0, R1;
   issue(R0);
   issue(R1);
-  if constexpr (ring_depth<D, KV8>() == 4) {
-    issue(R2);
-    issue(R3);
-  }
   __builtin_amdgcn_sched_barrier(0);
-  for (int u = 0; u < n_units; u += ring_depth<D, KV8>()) {
+  for (int u = 0; u < n_units; u += 2) {
     step(R0);
     __builtin_amdgcn_sched_barrier(0);
     issue(R0);
@@ -421,16 +415,6 @@ decode_split_kernel(const DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     issue(R1);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ring_depth<D, KV8>() == 4) {
-      step(R2);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(R2);
-      __builtin_amdgcn_sched_barrier(0);
-      step(R3);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(R3);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
 }
 

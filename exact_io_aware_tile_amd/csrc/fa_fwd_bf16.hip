@@ -67,14 +67,8 @@ constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 static_assert(kBr == kFwdRowsPerTileBf16, "host tiling must match");
 constexpr int kBc = 64;            // keys per tile
 constexpr int kStages = 4;         // LDS ring depth
-#ifndef FA_K_AHEAD
-#define FA_K_AHEAD 4
-#endif
-#ifndef FA_V_AHEAD
-#define FA_V_AHEAD 4
-#endif
-constexpr int kKAhead = FA_K_AHEAD;  // score-operand reads issued ahead of their MFMA
-constexpr int kVAhead = FA_V_AHEAD;  // P.V MFMAs whose operand reads are issued ahead
+constexpr int kKAhead = 4;  // score-operand reads issued ahead of their MFMA
+constexpr int kVAhead = 4;  // P.V MFMAs whose operand reads are issued ahead
 constexpr float kLazyBound = 65536.f;  // largest weight (2^16) formed against a stale reference
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));

@@ -25,10 +25,7 @@ namespace {
 
 constexpr int kMergeThreads = 256;
 constexpr int kGroup = 8;  // parts whose loads are in flight together
-#ifndef FA_MERGE_MAX_GRID
-#define FA_MERGE_MAX_GRID 65536
-#endif
-constexpr int64_t kMergeMaxGrid = FA_MERGE_MAX_GRID;  // workgroups; the rest is a grid-stride loop
+constexpr int64_t kMergeMaxGrid = 65536;  // workgroups; the rest is a grid-stride loop
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -373,7 +373,7 @@ int32_t fa_decode_paged_num_splits(const fa_decode_paged_args *args);
  * bytes (multiples of 16, token stride at most 2^26); the workspace size and
  * split count are reported by fa_decode_paged_fp8_workspace_size() and
  * fa_decode_paged_fp8_num_splits() (the automatic split count follows this
- * kernel's occupancy, three waves per SIMD below head_dim 256).  The codes are widened to
+ * kernel's occupancy, four waves per SIMD below head_dim 256).  The codes are widened to
  * bf16 exactly in registers and the products and softmax are those of
  * fa_decode_paged; K's descale scales the scores and V's the output.
  * Descale factors must be positive and finite.
