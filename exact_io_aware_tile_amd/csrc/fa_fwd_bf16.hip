@@ -43,6 +43,9 @@
 //     then is the tile's max taken, o and l rescaled and the weights
 //     recomputed.  Any reference gives the same o / l; fp32 and bf16 carry
 //     weights up to 2^16 without loss of relative precision.
+//   * o is divided by the sum of the weights as P.V took them (rounded to
+//     bf16), so each output row is a convex combination of value rows; the
+//     LSE uses the fp32 sum.
 //   * causal tiles above the diagonal are never visited; only tiles that
 //     straddle the diagonal or the sequence end are masked.
 //   * dropout (a compile-time variant, as "FlashAttention: The Algorithm That
@@ -180,7 +183,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // Dropout: this lane's row id, its index in the LSE layout.
   const uint64_t rid = (uint64_t)(lse_base + row);
   float m_run = -INFINITY;  // base-2 reference max of this lane's row
-  float l_run = 0.f;        // this half-wave's share of the running sum of weights
+  float l_run = 0.f;        // this half-wave's share of the running fp32 sum of weights (LSE)
+  float lb_run = 0.f;       // ... of the bf16-rounded weights P.V takes (normalises o)
   const float c = p.scale_log2;
 
   // DMA of one operand (K or V) of one tile into its LDS stage by the four
@@ -305,14 +309,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   float alpha = 1.f;
   // Weights p = 2^(s*c - m) of the tile for reference m: packed into the
   // bf16 B operands pf of the P.V product; this lane's sum of the fp32
-  // weights goes to ps.  When dma_tile >= 0 the wave's share of operand
+  // weights goes to ps, and of the rounded ones (v_dot2 with (1, 1) on the
+  // packed pairs, before any dropout) to pb.  When dma_tile >= 0 the wave's share of operand
   // DMA_V (K when false) of that tile is issued along the way, one
   // instruction per chunk: the vector-memory path takes about 15-30 cycles
   // per 1 KB instruction per CU and a wave stalls while it is busy, so the
   // loads are spaced out and issued only by the group whose matrix pipe is
   // idle.
-  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v, int32_t dma_phys) {
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  auto weights = [&](float m, float& ps, float& pb, int dma_tile, bool dma_v, int32_t dma_phys) {
     float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+    float pb2[2] = {0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       if (dma_tile >= 0 && kc % (4 / IPW) == 0) {
@@ -333,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       pw.y = pack_bf16x2(pv[2], pv[3]);
       pw.z = pack_bf16x2(pv[4], pv[5]);
       pw.w = pack_bf16x2(pv[6], pv[7]);
+      pb2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones2, pb2[0], false);
+      pb2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones2, pb2[1], false);
+      pb2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones2, pb2[0], false);
+      pb2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones2, pb2[1], false);
       if (DROP) {
         // Dropped weights become zero in P.V only; the sum keeps them.
         pw.x &= keep_mask16<0>(dw[kc][0], tm1);
@@ -343,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       pf[kc] = __builtin_bit_cast(bf16x8, pw);
     }
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    pb = pb2[0] + pb2[1];
   };
 
   // Dropout bytes of tile t into dw.  Both halves of the wave hold the same
@@ -384,8 +396,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     // sum (a large jump of the max, or no reference yet) sends the whole wave
     // to the exact step, which takes the row max, moves the reference and
     // recomputes the weights.
-    float ps;
-    weights(m_run, ps, dma_tile, dma_v, dma_phys);
+    float ps, pb;
+    weights(m_run, ps, pb, dma_tile, dma_v, dma_phys);
     corr = __any(!(ps <= kLazyBound));
     if (corr) {
       float mx[4];
@@ -399,10 +411,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       const float m_new = fmaxf(m_run, tmax);
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
+      lb_run *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false, 0);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb, -1, false, 0);
     }
     l_run += ps;
+    lb_run += pb;
   };
 
   // O^T += V^T P^T over four 16-key chunks of tile t.  Contraction slot j of
@@ -529,10 +543,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     }
   }
 
-  // Epilogue: O = o / l, LSE = (m + log2 l) * ln 2, with l the fp32 sum of
-  // the weights (P.V took them rounded to bf16).
+  // Epilogue: O = o / lb with lb the sum of the bf16-rounded weights P.V
+  // took, so each row is a convex combination of value rows up to fp32
+  // rounding (dividing by the fp32 sum instead would carry the rounding of
+  // a dominant weight, up to 2^-9 relative, into O); LSE = (m + log2 l) *
+  // ln 2 with the fp32 sum l.
   const float l_tot = sum_halves(l_run);
-  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? p.drop_scale : 1.f);
+  const float lb_tot = sum_halves(lb_run);
+  const float inv = (lb_tot > 0.f ? 1.f / lb_tot : 0.f) * (DROP ? p.drop_scale : 1.f);
   // The wave's 32 output rows go through LDS (the tile ring is idle: every
   // tile has been consumed behind the last barrier) so that global stores
   // write whole rows, 16 bytes per lane, instead of 8-byte pieces of 64

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   for (int i = 0; i < D / 16; ++i) oacc[i] = zero4();
   const uint64_t rid = (uint64_t)(lse_base + row);  // dropout row id (LSE layout)
   float m_run = -INFINITY;  // base-2 reference max of this lane's row
-  float l_run = 0.f;        // this lane's share of the running sum of weights
+  float l_run = 0.f;        // this lane's share of the running fp32 sum of weights (LSE)
+  float lb_run = 0.f;       // ... of the bf16-rounded weights P.V takes (normalises o)
   const float c = p.scale_log2;
 
   // DMA: wave w of the loading group covers rows 8(w%4) .. +7 of a tile,
@@ -267,8 +268,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   const uint32_t tm1 = DROP ? (uint32_t)(p.drop_t - 1) * 0x00010001u : 0u;
   bool corr = false;
   float alpha = 1.f;
-  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v, int32_t dma_phys) {
+  const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  auto weights = [&](float m, float& ps, float& pb, int dma_tile, bool dma_v, int32_t dma_phys) {
     float ps2[2] = {0.f, 0.f};
+    float pb2 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (dma_tile >= 0) {
@@ -285,6 +288,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
       }
       uint32_t w01 = pack_bf16x2(pv[0], pv[1]);
       uint32_t w23 = pack_bf16x2(pv[2], pv[3]);
+      pb2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w01), ones2, pb2, false);
+      pb2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w23), ones2, pb2, false);
       if (DROP) {
         w01 &= keep_mask16<0>(dw[kb], tm1);
         w23 &= keep_mask16<1>(dw[kb], tm1);
@@ -292,6 +297,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
       pf[kb] = __builtin_bit_cast(i16x4, make_uint2(w01, w23));
     }
     ps = ps2[0] + ps2[1];
+    pb = pb2;
   };
 
   auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
@@ -324,8 +330,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     // Fast path against the current reference (see the head_dim 64 / 128
     // kernel): a lane partial sum above the bound, infinite or NaN sends the
     // wave to the exact step.
-    float ps;
-    weights(m_run, ps, dma_tile, dma_v, dma_phys);
+    float ps, pb;
+    weights(m_run, ps, pb, dma_tile, dma_v, dma_phys);
     corr = __any(!(ps <= kLazyBound));
     if (corr) {
       float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
@@ -335,10 +341,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
       const float m_new = fmaxf(m_run, tmax);
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
+      lb_run *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false, 0);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb, -1, false, 0);
     }
     l_run += ps;
+    lb_run += pb;
   };
 
   // O^T += V^T P^T over both 16-key blocks of tile t in one product per
@@ -443,11 +451,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     }
   }
 
-  // Epilogue: O = o / l (times the dropout keep scale), LSE = (m + log2 l)
-  // ln 2, with l the fp32 sum of the weights over the row's four lanes.
+  // Epilogue: O = o / lb (times the dropout keep scale), LSE = (m + log2 l)
+  // ln 2, with l and lb summed over the row's four lanes.
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot = sum_halves(l_tot);
-  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? p.drop_scale : 1.f);
+  // o is divided by the sum of the weights as P.V took them (bf16): each row
+  // is a convex combination of value rows; the LSE uses the fp32 sum.
+  float lb_tot = lb_run + __shfl_xor(lb_run, 16, 64);
+  lb_tot = sum_halves(lb_tot);
+  const float inv = (lb_tot > 0.f ? 1.f / lb_tot : 0.f) * (DROP ? p.drop_scale : 1.f);
   // The wave's 16 output rows go through its 8 KB share of the idle K ring
   // (16-byte chunks of each row swizzled by the row) so that global stores
   // write whole rows.

@@ -375,9 +375,11 @@ def test_prefill_full_size_properties(gpu):
     vf = v.float()
     vmin = torch.cummin(vf, dim=1).values  # causal: keys 0..i
     vmax = torch.cummax(vf, dim=1).values
-    # The exact row lies in the hull; the bf16 contract allows max |dO| of
-    # TOL["bf16"][0], so the GPU row lies within the hull widened by that.
-    slack = TOL["bf16"][0]
+    # o is divided by the sum of the weights P.V took, so the fp32 row is a
+    # convex combination of value rows up to fp32 rounding, and rounding it
+    # to bf16 (monotone, the hull's bounds being bf16 values) cannot leave
+    # the hull: only fp32 rounding noise is allowed.
+    slack = 1e-3
     assert bool((of >= vmin - slack).all()) and bool((of <= vmax + slack).all())
     # LSE >= the row's own diagonal score (that key is always visible)
     diag = (q.float() * k.float()).sum(-1) / math.sqrt(case["d"])  # [B, N, H]
