@@ -493,8 +493,10 @@ FA_EXPORT int32_t fa_decode_paged_fp8_num_splits(const fa_decode_paged_fp8_args*
 
 namespace {
 // Paged decode over bf16 pools, or E4M3 pools (kv8) with descale factors.
+// no_alloc: the partial states go to the library's own per-device scratch
+// array instead of the caller's workspace (whose fields are then ignored).
 fa_status decode_impl(const fa_decode_paged_args* a, bool kv8, float k_descale, float v_descale, const char* fn,
-                      void* stream) {
+                      void* stream, bool no_alloc = false) {
   const fa_status st = check_decode(a);
   if (st != FA_OK) return st;
   if (!(a->scale > 0.f) || !std::isfinite(a->scale))
@@ -502,7 +504,7 @@ fa_status decode_impl(const fa_decode_paged_args* a, bool kv8, float k_descale, 
   if (kv8 && (!(k_descale > 0.f) || !std::isfinite(k_descale) || !(v_descale > 0.f) || !std::isfinite(v_descale)))
     return fail(FA_ERR_BAD_SHAPE, "%s: descale factors must be positive and finite", fn);
   if (a->batch == 0) return ok();
-  if (!a->q || !a->seq_lens || !a->o || !a->workspace)
+  if (!a->q || !a->seq_lens || !a->o || (!no_alloc && !a->workspace))
     return fail(FA_ERR_NULL_POINTER, "%s: q, seq_lens, o and workspace are required", fn);
   if (a->max_seq_len > 0 && (!a->k_pool || !a->v_pool || !a->block_table))
     return fail(FA_ERR_NULL_POINTER, "%s: pools and block_table are required when max_seq_len > 0", fn);
@@ -510,13 +512,23 @@ fa_status decode_impl(const fa_decode_paged_args* a, bool kv8, float k_descale, 
   if (!strides_ok(a->pool_stride, 3, kv8 ? 16 : 8) || !strides_ok(a->q_stride, 2, 8) || !strides_ok(a->o_stride, 2, 8))
     return fail(FA_ERR_BAD_SHAPE, "%s: strides must be non-negative multiples of 16 bytes", fn);
   if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->o) ||
-      !aligned16(a->workspace))
+      (!no_alloc && !aligned16(a->workspace)))
     return fail(FA_ERR_BAD_SHAPE, "%s: q, pools, o and workspace must be 16-byte aligned", fn);
   const int parts = decode_parts(a, kv8);
   if (parts < 1) return fail(FA_ERR_HIP, "%s: cannot query the current device", fn);
   const size_t need = fa::decode_workspace_bytes(parts, a->batch, a->heads_q, a->head_dim);
-  if (a->workspace_bytes < need)
+  void* ws = a->workspace;
+  if (no_alloc) {
+    if (need > fa::kDecodeScratchBytes)
+      return fail(FA_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: these arguments need %zu bytes of partial states, the library holds %zu (lower num_splits "
+                  "or the batch, or call fa_decode_paged with a workspace)",
+                  fn, need, fa::kDecodeScratchBytes);
+    const hipError_t e = fa::decode_scratch(&ws);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(e));
+  } else if (a->workspace_bytes < need) {
     return fail(FA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn, a->workspace_bytes, need);
+  }
 
   fa::DecodeParams p{};
   p.q = a->q;
@@ -531,7 +543,7 @@ fa_status decode_impl(const fa_decode_paged_args* a, bool kv8, float k_descale, 
   p.lse = a->lse;
   p.num_splits = parts;
   const size_t rows = (size_t)a->heads_q * (size_t)(parts + a->batch);
-  p.ws_o = (float*)a->workspace;
+  p.ws_o = (float*)ws;
   p.ws_ml = p.ws_o + rows * a->head_dim;
   p.batch = a->batch;
   p.heads_q = a->heads_q;
@@ -551,6 +563,12 @@ fa_status decode_impl(const fa_decode_paged_args* a, bool kv8, float k_descale, 
 FA_EXPORT fa_status fa_decode_paged(const fa_decode_paged_args* a, void* stream) {
   return decode_impl(a, false, 1.f, 1.f, "fa_decode_paged", stream);
 }
+
+FA_EXPORT fa_status fa_decode_paged_noalloc(const fa_decode_paged_args* a, void* stream) {
+  return decode_impl(a, false, 1.f, 1.f, "fa_decode_paged_noalloc", stream, true);
+}
+
+FA_EXPORT size_t fa_decode_paged_noalloc_max_bytes(void) { return fa::kDecodeScratchBytes; }
 
 FA_EXPORT fa_status fa_decode_paged_fp8(const fa_decode_paged_fp8_args* a, void* stream) {
   if (!a) return fail(FA_ERR_NULL_POINTER, "fa_decode_paged_fp8: args is NULL");

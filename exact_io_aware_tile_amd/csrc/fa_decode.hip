@@ -54,11 +54,19 @@
 // 16-byte K load then covers two score steps: the contraction is relabelled
 // so that step 2u + h takes head dims 64u + 16(l/16) + 8h .. +7 (Q is loaded
 // with the same relabelling).
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
+
+// Device memory of the allocation-free decode entry point: the split
+// kernel's partial states live here instead of in a caller workspace.  One
+// copy per GPU, held until the process ends; every call on a GPU reuses it,
+// so calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 constexpr int kBlock = 16;
 constexpr float kLazyLog2 = 8.f;    // largest weight 2^8 against a stale reference
@@ -523,6 +531,27 @@ int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_
   if (parts > (max_units + 3) / 4) parts = (max_units + 3) / 4;
   if (parts < 1) parts = 1;
   return (int)parts;
+}
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDecodeScratchMaxDevices) return hipErrorInvalidDevice;
+  // The array's name is a host-side stand-in: its device address is looked
+  // up once per device, with that device current, and used from then on.
+  static std::mutex mu;
+  static void* addr[kDecodeScratchMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim) {

@@ -105,6 +105,11 @@ hipError_t launch_decode_paged(const DecodeParams& p, int head_dim, hipStream_t 
 // device, or of a 256-CU device when none can be queried).
 int decode_num_parts(int num_splits, int batch, int heads_q, int group, int max_seq_len, int head_dim, bool kv8);
 size_t decode_workspace_bytes(int parts, int batch, int heads_q, int head_dim);
+// Library-held decode workspace (one per device, for callers that cannot
+// allocate): its size, and its address on the current device.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+constexpr int kDecodeScratchMaxDevices = 64;
+hipError_t decode_scratch(void** ptr);
 
 // Merge of P partial (o, lse) states of the same rows.
 struct MergeParams {

@@ -108,7 +108,8 @@ class MergeStatesArgs(ctypes.Structure):
 
 SYMBOLS = ("fa_fwd", "fa_fwd_dropout", "fa_fwd_fp8", "fa_fwd_varlen", "fa_fwd_varlen_dropout", "fa_fwd_varlen_fp8", "fa_fwd_paged", "fa_fwd_paged_fp8", "fa_decode_paged", "fa_decode_paged_workspace_size",
            "fa_decode_paged_num_splits", "fa_decode_paged_fp8", "fa_decode_paged_fp8_workspace_size",
-           "fa_decode_paged_fp8_num_splits", "fa_merge_states", "fa_status_string", "fa_last_error", "fa_abi_version")
+           "fa_decode_paged_fp8_num_splits", "fa_decode_paged_noalloc", "fa_decode_paged_noalloc_max_bytes",
+           "fa_merge_states", "fa_status_string", "fa_last_error", "fa_abi_version")
 
 _lib = None
 
@@ -150,6 +151,10 @@ def load(path: str):
     L.fa_fwd_paged.restype = ctypes.c_int
     L.fa_decode_paged.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
     L.fa_decode_paged.restype = ctypes.c_int
+    L.fa_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodePagedArgs), _P]
+    L.fa_decode_paged_noalloc.restype = ctypes.c_int
+    L.fa_decode_paged_noalloc_max_bytes.argtypes = []
+    L.fa_decode_paged_noalloc_max_bytes.restype = ctypes.c_size_t
     L.fa_fwd_paged_fp8.argtypes = [ctypes.POINTER(FwdPagedFp8Args), _P]
     L.fa_fwd_paged_fp8.restype = ctypes.c_int
     L.fa_decode_paged_fp8.argtypes = [ctypes.POINTER(DecodePagedFp8Args), _P]
@@ -574,6 +579,22 @@ def fa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check(lib().fa_decode_paged(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def fa_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, max_seq_len: int, *,
+                            scale: float | None = None, num_splits: int = 0, out, lse=None, stream=None):
+    """Paged single-token decode that allocates nothing: the caller passes
+    ``out`` (and optionally ``lse``); the partial states go to the library's
+    own per-device workspace.  Returns (out, lse)."""
+    torch = _torch()
+    _check_decode(q, k_pool, v_pool, block_table, seq_lens, out, lse, None, torch.bfloat16)
+    _dev(q, k_pool, v_pool, block_table, seq_lens, out, lse)
+    a = _decode_args(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, scale, num_splits)
+    a.o, a.lse = _ptr(out), _ptr(lse)
+    a.o_stride[:] = list(out.stride()[:2])
+    a.workspace, a.workspace_bytes = None, 0
+    _check(lib().fa_decode_paged_noalloc(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

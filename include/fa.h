@@ -25,7 +25,8 @@
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library never allocates, frees or retains them, and keeps no state
- *     between calls.
+ *     between calls (fa_decode_paged_noalloc's fixed per-device workspace
+ *     holds only intermediate values of one call).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on that stream and returns; nothing
  *     synchronises.  Faults during execution surface at the caller's next
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 9
+#define FA_ABI_VERSION 10
 
 typedef enum {
   FA_OK = 0,
@@ -364,6 +365,36 @@ fa_status fa_decode_paged(const fa_decode_paged_args *args, void *stream);
 /* The number of parts fa_decode_paged will cut each KV head's key blocks
  * into for these arguments (0 on invalid arguments). */
 int32_t fa_decode_paged_num_splits(const fa_decode_paged_args *args);
+
+/*
+ * fa_decode_paged_noalloc -- fa_decode_paged for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results (bit for
+ * bit, for the same arguments and split count), with the partial states kept
+ * in a workspace the library itself holds instead of the caller's.
+ *
+ *   args: as for fa_decode_paged; `workspace` and `workspace_bytes` are
+ *       ignored.  Inputs and outputs are still the caller's.
+ *   The library's workspace is a fixed array of
+ *       fa_decode_paged_noalloc_max_bytes() bytes (16 MiB) in device memory,
+ *       one per GPU the library runs on, held until the process ends.  Its
+ *       address is looked up on the first call on each device (the current
+ *       device; `stream` must belong to it).  Arguments whose
+ *       fa_decode_paged_workspace_size() exceeds it are rejected with
+ *       FA_ERR_WORKSPACE_TOO_SMALL before any launch (lower num_splits or
+ *       the batch, or call fa_decode_paged with a workspace).
+ *   Nothing is allocated or freed: no hipMalloc, hipFree or allocating
+ *       library call.  Nothing needs clearing between calls (the kernels
+ *       write every partial state they read).
+ *   Every call on one GPU shares that GPU's array: calls that overlap in
+ *       time on one GPU (different streams without ordering between them,
+ *       or different host threads) race and give undefined results.
+ *       Calls ordered on one stream are safe.
+ */
+fa_status fa_decode_paged_noalloc(const fa_decode_paged_args *args, void *stream);
+
+/* Bytes of the library-held workspace of fa_decode_paged_noalloc. */
+size_t fa_decode_paged_noalloc_max_bytes(void);
 
 /*
  * fa_decode_paged_fp8 -- fa_decode_paged over an FP8 KV cache: k_pool and

@@ -56,7 +56,7 @@ def test_no_unresolved_library_symbols():
 def test_abi_version_and_strings(L):
     with open(os.path.join(ROOT, "include", "fa.h")) as f:
         declared = int(re.search(r"#define FA_ABI_VERSION (\d+)", f.read()).group(1))
-    assert L.fa_abi_version() == declared == 9
+    assert L.fa_abi_version() == declared == 10
     for st in range(6):
         assert L.fa_status_string(st)
     assert L.fa_status_string(0) == b"ok"
@@ -469,6 +469,28 @@ def test_decode_sizes(L):
     bad = decode_args(head_dim=96)
     assert L.fa_decode_paged_workspace_size(ctypes.byref(bad)) == 0
     assert L.fa_decode_paged_num_splits(ctypes.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads_q=30), fa.FA_ERR_BAD_SHAPE),
+    (dict(head_dim=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(block_table=None), fa.FA_ERR_NULL_POINTER),
+    (dict(o=None), fa.FA_ERR_NULL_POINTER),
+    # 64 sequences x 32 heads x (1000 + 64) slots x 132 floats: 36 MB > 16 MiB
+    (dict(num_splits=1000, batch=64, max_seq_len=64 * 16), fa.FA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_noalloc_rejects_before_launch(L, kw, status):
+    a = decode_args(**kw)
+    a.workspace, a.workspace_bytes = None, 0
+    assert L.fa_decode_paged_noalloc(ctypes.byref(a), None) == status
+    assert L.fa_last_error()
+
+
+def test_decode_noalloc_limit(L):
+    assert L.fa_decode_paged_noalloc_max_bytes() == 16 << 20
+    # the batch-64 decode workload with its automatic split fits
+    a = decode_args(batch=64, max_seq_len=32768, max_blocks_per_seq=2048)
+    assert 0 < L.fa_decode_paged_workspace_size(ctypes.byref(a)) <= L.fa_decode_paged_noalloc_max_bytes()
 
 
 def test_decode_empty_batch_is_noop(L):
