@@ -18,9 +18,10 @@
 //     (global_load_lds, 16 bytes per lane, no register staging) through a
 //     ring of 4 stages.  Rows are stored whole (d contiguous) with the 16-byte
 //     chunks of each row XOR-swizzled so that both the score-operand reads and
-//     the transposed value reads hit distinct banks.  Only the waves in their
-//     softmax phase issue loads, spread over the softmax: a wave stalls while
-//     the CU's vector-memory path is busy, and the MFMA waves must not.
+//     the transposed value reads hit distinct banks.  The waves in their
+//     MFMA phase issue the loads, spread between the products: a load that
+//     waits for the CU's vector-memory path delays the next product only by
+//     what the matrix pipe has not yet absorbed of the one before it.
 //   * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16,
 //     so each lane's accumulator column is ONE query row: the row max and row
 //     sum are in-lane reductions plus one v_permlane32_swap, and the
@@ -58,6 +59,8 @@
 //   * the first-tile NaN of "exp(-inf - -inf)" ("S12 FlashAttention", "Build
 //     it / Implementation") is avoided by substituting 0 for a -inf reference
 //     when forming exponents.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -70,8 +73,6 @@ constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 static_assert(kBr == kFwdRowsPerTileBf16, "host tiling must match");
 constexpr int kBc = 64;            // keys per tile
 constexpr int kStages = 4;         // LDS ring depth
-constexpr int kKAhead = 4;  // score-operand reads issued ahead of their MFMA
-constexpr int kVAhead = 4;  // P.V MFMAs whose operand reads are issued ahead
 constexpr float kLazyBound = 65536.f;  // largest weight (2^16) formed against a stale reference
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -265,35 +266,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i, phys);
   };
 
-  // Prologue loads: group 0 takes K, group 1 V.  Tile 0 flies while the Q
-  // fragments arrive.
-  if (nt > 0) dma_op(0, grp != 0);
+  // Group 0 loads the key tiles, group 1 the value tiles.  Tile 0 flies
+  // while the Q fragments arrive.
+  const bool v_loader = grp != 0;
+  if (nt > 0) dma_op(0, v_loader);
 
-  // Scores of one tile (S^T, two 32-key blocks).
-  f32x16 sacc[2];
-  auto scores = [&](int t) {
-    const uint16_t* ks = &k_s[t % kStages][0];
-    sacc[0] = zero16();
-    sacc[1] = zero16();
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + l32;
-        const uint4 a = *(const uint4*)&ks[r * D + swz_k(CH, r, 2 * kk + hi) * 8];
-        sacc[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[kk], sacc[kb]);
-      }
-    }
-    // Keep kKAhead operand reads in flight ahead of the MFMAs (LDS latency
-    // is several MFMAs long).
-    __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
-#pragma unroll
-    for (int i = 0; i < D / 8 - kKAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
-  };
+  f32x16 sacc[2];  // S^T of one tile: two 32-key blocks
 
   // Softmax of tile t in place (scores -> weights), producing the bf16 B
   // operands of the P.V product.
@@ -303,30 +281,19 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // (words hi and 2 + hi of the generator's output for the 16-key group kc).
   uint32_t dw[4][2];
   const uint32_t tm1 = DROP ? (uint32_t)(p.drop_t - 1) * 0x00010001u : 0u;
-  // The correction of o found by a softmax is applied at the start of the
-  // following P.V phase (o is not touched in between); l is corrected at once.
-  bool corr = false;   // the reference moved in the last softmax: o must be scaled by alpha
-  float alpha = 1.f;
+  // When a softmax moves the reference, o and l are rescaled by alpha right
+  // there, in the vector-ALU phase (o was last written by the P.V products
+  // of the MFMA phase before it).
   // Weights p = 2^(s*c - m) of the tile for reference m: packed into the
   // bf16 B operands pf of the P.V product; this lane's sum of the fp32
   // weights goes to ps, and of the rounded ones (v_dot2 with (1, 1) on the
-  // packed pairs, before any dropout) to pb.  When dma_tile >= 0 the wave's share of operand
-  // DMA_V (K when false) of that tile is issued along the way, one
-  // instruction per chunk: the vector-memory path takes about 15-30 cycles
-  // per 1 KB instruction per CU and a wave stalls while it is busy, so the
-  // loads are spaced out and issued only by the group whose matrix pipe is
-  // idle.
+  // packed pairs, before any dropout) to pb.
   const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-  auto weights = [&](float m, float& ps, float& pb, int dma_tile, bool dma_v, int32_t dma_phys) {
+  auto weights = [&](float m, float& ps, float& pb) {
     float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-    float pb2[2] = {0.f, 0.f};
+    float pb4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      if (dma_tile >= 0 && kc % (4 / IPW) == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        dma_one(dma_tile, dma_v, kc / (4 / IPW), dma_phys);
-        __builtin_amdgcn_sched_barrier(0);
-      }
       const int kb = kc >> 1;
       const int r0 = 8 * (kc & 1);
       float pv[8];
@@ -340,10 +307,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       pw.y = pack_bf16x2(pv[2], pv[3]);
       pw.z = pack_bf16x2(pv[4], pv[5]);
       pw.w = pack_bf16x2(pv[6], pv[7]);
-      pb2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones2, pb2[0], false);
-      pb2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones2, pb2[1], false);
-      pb2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones2, pb2[0], false);
-      pb2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones2, pb2[1], false);
+      pb4[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones2, pb4[0], false);
+      pb4[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones2, pb4[1], false);
+      pb4[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones2, pb4[2], false);
+      pb4[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones2, pb4[3], false);
       if (DROP) {
         // Dropped weights become zero in P.V only; the sum keeps them.
         pw.x &= keep_mask16<0>(dw[kc][0], tm1);
@@ -354,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       pf[kc] = __builtin_bit_cast(bf16x8, pw);
     }
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
-    pb = pb2[0] + pb2[1];
+    pb = (pb4[0] + pb4[1]) + (pb4[2] + pb4[3]);
   };
 
   // Dropout bytes of tile t into dw.  Both halves of the wave hold the same
@@ -378,17 +345,20 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     }
   };
 
-  auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
+  auto softmax = [&](int t) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
     if (need_mask) {
       const int lim = CAUSAL ? row + off : nk - 1;
       const int kend = (nk - 1 < lim ? nk - 1 : lim) - k0 - 4 * hi;
+      // One compare and one select per score (a key past kend is masked).
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > kend) sacc[kb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[kb][r];
+          sacc[kb][r] = kb * 32 + 8 * (r >> 2) + (r & 3) <= kend ? x : -INFINITY;
+        }
     }
     // Fast path: weights against the current reference m_run, without the
     // tile's row max.  Every weight is at most this lane's partial sum, so a
@@ -397,9 +367,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     // to the exact step, which takes the row max, moves the reference and
     // recomputes the weights.
     float ps, pb;
-    weights(m_run, ps, pb, dma_tile, dma_v, dma_phys);
-    corr = __any(!(ps <= kLazyBound));
-    if (corr) {
+    weights(m_run, ps, pb);
+    if (__any(!(ps <= kLazyBound))) {
       float mx[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -409,137 +378,235 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       }
       const float tmax = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * c;
       const float m_new = fmaxf(m_run, tmax);
-      alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
       lb_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb, -1, false, 0);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb);
     }
     l_run += ps;
     lb_run += pb;
   };
 
+  // The MFMA phase of tile t is one stream of products: the NPV products
+  // O^T += V^T P^T of tile t, then (when tile t + 1 exists) the NSC score
+  // products S^T = K Q^T of tile t + 1.  Product i's LDS operand reads are
+  // issued kPre products ahead of it, and the reads of the first kPre
+  // products (values of tile t, visible since two phases) are issued at the
+  // end of the softmax phase before, so the phase opens on a product instead
+  // of on the LDS latency, and no latency gap opens between the two halves.
+  //
   // O^T += V^T P^T over four 16-key chunks of tile t.  Contraction slot j of
   // lane half hi is key 16*kc + 4*hi + j (j < 4) or 16*kc + 8 + 4*hi + (j-4):
   // exactly the keys the lane's score registers 8*(kc%2) .. +7 hold.  The two
   // transposed reads return those 8 keys for d = 32*db + l%32: lane (4k + q)
   // of each 16-lane group points at key row (base + k), dims
-  // (16-block + 4q .. +3).
+  // (16-block + 4q .. +3).  Score product j = 2 kk + kb reads key rows
+  // 32 kb + l%32, head dims 16 kk + 8 hi .. +7 of tile t + 1.
+  constexpr int NPV = 4 * (D / 32);
+  constexpr int NSC = 2 * (D / 16);
+  constexpr int kPre = 6;  // products whose operand reads are in flight ahead
   const int g16 = lane >> 4;
   const int tk = (lane >> 2) & 3;
   const int tq = lane & 3;
-  auto pv = [&](int t) {
-    if (corr) {
+  uint4 opa[NPV + NSC];
+  // Value reads: the swizzle of key rows 16 kc + 4 hi + tk (+ 8) depends on
+  // tk only, so each 32-dim block db has one per-lane LDS address for stage
+  // 0; chunk kc, the upper 8 keys and the stage add uniform offsets.
+  uint32_t vbase[D / 32];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+  for (int db = 0; db < D / 32; ++db) {
+    const int dc = 4 * db + 2 * (g16 & 1) + (tq >> 1);  // logical 16-byte chunk
+    const int ka = 4 * hi + tk;
+    vbase[db] = (uint32_t)(uintptr_t)&v_s[0][0] + 2u * (uint32_t)(ka * D + swz_v(CH, ka, dc) * 8 + 4 * (tq & 1));
+  }
+  auto read_op = [&](int i, int t) {
+    if (i < NPV) {
+      const int kc = i / (D / 32), db = i % (D / 32);
+      const uint32_t a = vbase[db] + 2u * (uint32_t)((t % kStages) * TILE) + 2u * (uint32_t)(16 * kc * D);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a);
+      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a + 2u * 8u * D));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo);
+      const uint2 u2 = __builtin_bit_cast(uint2, up);
+      opa[i] = make_uint4(l2.x, l2.y, u2.x, u2.y);
+    } else {
+      const uint16_t* ks = &k_s[(t + 1) % kStages][0];
+      const int kk = (i - NPV) >> 1, kb = (i - NPV) & 1;
+      const int r = kb * 32 + l32;
+      opa[i] = *(const uint4*)&ks[r * D + swz_k(CH, r, 2 * kk + hi) * 8];
     }
-    const uint16_t* vs = &v_s[t % kStages][0];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int dc = 4 * db + 2 * (g16 & 1) + (tq >> 1);  // logical 16-byte chunk
-        const int ka = 16 * kc + 4 * hi + tk;
-        const int kb2 = ka + 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)&vs[ka * D + swz_v(CH, ka, dc) * 8 + 4 * (tq & 1)]);
-        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)&vs[kb2 * D + swz_v(CH, kb2, dc) * 8 + 4 * (tq & 1)]);
-        const uint2 l2 = __builtin_bit_cast(uint2, lo);
-        const uint2 u2 = __builtin_bit_cast(uint2, up);
-        const uint4 a = make_uint4(l2.x, l2.y, u2.x, u2.y);
-        oacc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[kc], oacc[db]);
-      }
-    }
-    // Two transposed reads per MFMA; kVAhead MFMAs' worth in flight.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
-#pragma unroll
-    for (int i = 0; i < D / 8 - kVAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
   };
+  auto mfma_op = [&](int i) {
+    if (i < NPV) {
+      const int kc = i / (D / 32), db = i % (D / 32);
+      oacc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, opa[i]), pf[kc], oacc[db]);
+    } else {
+      const int kk = (i - NPV) >> 1, kb = (i - NPV) & 1;
+      sacc[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, opa[i]), qf[kk], kk == 0 ? zero16() : sacc[kb]);
+    }
+  };
+  // Reads of the first kPre products of tile t's phase, at the end of the
+  // softmax phase before it (only the value tile, already visible, is read).
+  auto prefetch = [&](int t) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) read_op(i, t);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The products of tile t (and the scores of tile t + 1 when NEXT).  When
+  // dma_tile >= 0, this wave's share of that tile's operand (values for
+  // group 1, keys for group 0) is issued along the way, one LDS-DMA
+  // instruction after every N / IPW products: the CU's vector-memory path
+  // takes a 1 KB instruction every ~16 cycles, so an instruction may wait
+  // to issue while the matrix pipe works through the product before it.
+  auto mfma_phase = [&](int t, auto next, int dma_tile, int32_t dma_phys) {
+    constexpr int N = decltype(next)::value ? NPV + NSC : NPV;
+    constexpr int DSTEP = N / IPW;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      mfma_op(i);
+      if (i + kPre < N) read_op(i + kPre, t);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kPre < NPV)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed value reads
+      else if (i + kPre < N)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one key read
+      if (i % DSTEP == DSTEP / 2 && dma_tile >= 0) dma_one(dma_tile, v_loader, i / DSTEP, dma_phys);
+    }
+  };
+  // The scores of tile 0 (the first MFMA phase), kPre reads ahead.
+  auto scores0 = [&]() {
+#pragma unroll
+    for (int i = NPV; i < NPV + NSC; ++i) {
+      if (i == NPV) {
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) read_op(NPV + j, -1);
+      }
+      mfma_op(i);
+      if (i + kPre < NPV + NSC) read_op(i + kPre, -1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+    for (int i = NPV; i < NPV + NSC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kPre < NPV + NSC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  const std::integral_constant<bool, true> with_next{};
+  const std::integral_constant<bool, false> last{};
 
   // Phase schedule.  Global phases P = 0 .. 2*nt + 1, each ended by a
-  // workgroup barrier.  Group 0 runs the MFMA phase of tile t (the scores of
-  // tile t, then P.V of tile t - 1) in phase 2t and the softmax of tile t in
-  // phase 2t + 1; group 1 runs the same sequence one phase later.  Scores go
-  // first so that the next softmax waits only for them, not for the P.V
-  // products queued behind them on the matrix pipe.  So K of tile t is read
-  // in phases 2t and 2t + 1, V of tile t in phases 2t + 2 and 2t + 3.
+  // workgroup barrier.  Group 0 runs the scores of tile 0 in phase 0, then
+  // for each tile t the softmax of tile t in phase 2t + 1 (closing with the
+  // prefetch of tile t's first value operands) and the MFMA phase of tile t
+  // (P.V of tile t, scores of tile t + 1) in phase 2t + 2; group 1 runs the
+  // same sequence one phase later.  So K of tile t is read in phases 2t and
+  // 2t + 1, V of tile t in phases 2t + 1 .. 2t + 3.
   //
-  // Loads come from the group in its softmax phase, one operand of one tile
-  // per phase, into stage t % 4: K of tile t in phase 2t - 4 by group 1 (K of
-  // tile t - 4 was last read in phase 2t - 7), V of tile t in phase 2t - 3 by
-  // group 0 (V of tile t - 4 was last read in phase 2t - 5).  The prologue
-  // loads tiles 0 and 1 (group 0 K, group 1 V).  At the end of odd phase P
-  // each wave waits for its share of tile (P+1)/2, which group 0 reads next;
-  // only its share of the following tile, issued later, may still be in
-  // flight.  The two groups' loops are written out separately so every phase
-  // is straight-line code.
+  // Loads into stage t % 4, from the group in its MFMA phase (whose matrix
+  // pipe hides the issue cost): K of tile t + 4 by group 0 in phase 2t + 2
+  // (K of tile t was last read in phase 2t + 1), V of tile t + 3 by group 1
+  // in phase 2t + 3 (V of tile t - 1 was last read in phase 2t + 1).  The
+  // prologue loads K of tiles 0 .. 3 and V of tiles 0 .. 2.  At the end of odd
+  // phase 2s - 1 each wave waits for its share of tile s, which group 0 reads
+  // next: of its own later loads, K of tiles s + 1 and s + 2 (group 0) or V
+  // of tile s + 1 (group 1) may still be in flight.  The two groups' loops
+  // are written out separately so every phase is straight-line code.
+  auto wait_tiles_in_flight = [&](int n) {  // n later tiles of this wave may fly
+    if (n <= 0)
+      wait_vmcnt<0>();
+    else if (n == 1)
+      wait_vmcnt<IPW>();
+    else
+      wait_vmcnt<2 * IPW>();
+  };
   auto phase_end = [&](int P) {
     if (P & 1) {
-      const int t_need = (P + 1) / 2;
-      if (t_need < nt) {
-        if (t_need + 1 < nt)
-          wait_vmcnt<IPW>();
-        else
-          wait_vmcnt<0>();
+      const int s_need = (P + 1) / 2;
+      if (s_need < nt) {
+        const int last_issued = v_loader ? min(s_need + 1, nt - 1) : min(s_need + 2, nt - 1);
+        wait_tiles_in_flight(last_issued - s_need);
       }
     }
     lds_barrier();
   };
   if (nt > 0) {
     // The Q loads were issued before tile 0's DMA (the DMA asm is a memory
-    // barrier for the compiler); wait for both, then let tile 1 fly.
+    // barrier for the compiler); wait for both, then let the next tiles fly.
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
     wait_vmcnt<0>();
-    if (nt > 1) dma_op(1, grp != 0);
+    for (int j = 1; j < (v_loader ? 3 : 4) && j < nt; ++j) dma_op(j, v_loader);
     lds_barrier();
-    // Paged: the table entry for the DMA of the next softmax phase is read
-    // at the end of the MFMA phase before it, when no LDS read is pending
-    // (both count on the same counter), and arrives during the barrier.
+    // Paged: the table entry for the next MFMA phase's DMA is read through
+    // the scalar cache at the start of the softmax phase before it, when no
+    // LDS read is pending (both count on the same counter), and is waited
+    // for before that phase's prefetch reads are issued.
+    auto table_entry = [&](int tile) {
+      const int32_t e = pool_block(tile);
+      return e;
+    };
+    auto settle = [&](int32_t& e) {
+      if (PAGED) asm volatile("" : "+s"(e));
+    };
+    // The last tile's MFMA phase has no scores of a next tile; it is peeled
+    // off the loop so that the loop body is one straight stream.
     if (grp == 0) {
-      scores(0);
+      scores0();
       if (DROP) draw(0);
-      int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
-      for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 2 < nt ? t + 2 : -1, true, ph);
+      for (int t = 0; t < nt - 1; ++t) {
+        int32_t ph = table_entry(t + 4 < nt ? t + 4 : -1);
+        softmax(t);
+        settle(ph);
+        prefetch(t);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < nt) scores(t + 1);
-        if (DROP && t + 1 < nt) draw(t + 1);
-        pv(t);
+        if (DROP) draw(t + 1);
+        mfma_phase(t, with_next, t + 4 < nt ? t + 4 : -1, ph);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
-        ph = pool_block(t + 3 < nt ? t + 3 : -1);
         phase_end(2 * t + 2);
       }
+      softmax(nt - 1);
+      prefetch(nt - 1);
+      phase_end(2 * nt - 1);
+      __builtin_amdgcn_s_setprio(1);
+      mfma_phase(nt - 1, last, -1, 0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      phase_end(2 * nt);
       phase_end(2 * nt + 1);
     } else {
-      if (2 < nt) dma_op(2, false);
-      int32_t ph = pool_block(3 < nt ? 3 : -1);
       phase_end(0);
-      scores(0);
+      scores0();
       if (DROP) draw(0);
       phase_end(1);
-      for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 3 < nt ? t + 3 : -1, false, ph);
+      for (int t = 0; t < nt - 1; ++t) {
+        int32_t ph = table_entry(t + 3 < nt ? t + 3 : -1);
+        softmax(t);
+        settle(ph);
+        prefetch(t);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < nt) scores(t + 1);
-        if (DROP && t + 1 < nt) draw(t + 1);
-        pv(t);
+        if (DROP) draw(t + 1);
+        mfma_phase(t, with_next, t + 3 < nt ? t + 3 : -1, ph);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
-        ph = pool_block(t + 4 < nt ? t + 4 : -1);
         phase_end(2 * t + 3);
       }
+      softmax(nt - 1);
+      prefetch(nt - 1);
+      phase_end(2 * nt);
+      __builtin_amdgcn_s_setprio(1);
+      mfma_phase(nt - 1, last, -1, 0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      phase_end(2 * nt + 1);
     }
   }
 
