@@ -261,9 +261,11 @@ def oracle_leg(legs, seconds):
                 errs.append((o_rows[rows], l_rows[rows], o_ref, l_ref))
             el = time.perf_counter() - t0
             n_rows = int(sum(r.size for r in done))
+            n_distinct = int(np.unique(np.concatenate(done)).size)
             base = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                    "sample": f"{n_rows} query rows drawn uniformly from the workload's {B * H * N} "
-                              f"(b, h, i) rows, fp64 materialised-score oracle, {el:.1f} s wall"}
+                    "sample": f"{n_rows} query rows ({n_distinct} distinct) drawn uniformly with replacement, "
+                              f"256 at a time, from the workload's {B * H * N} (b, h, i) rows, plus each batch's "
+                              f"tile-edge rows; fp64 materialised-score oracle, {el:.1f} s wall"}
             parity[key] = parity_stats(*(np.concatenate([e[i] for e in errs]) for i in range(4)))
         elif key == "long":
             B, N, H, d = case["batch"], case["nq"], case["hq"], case["d"]
