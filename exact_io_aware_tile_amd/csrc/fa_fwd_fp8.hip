@@ -227,7 +227,10 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     for (int i = 0; i < IPW; ++i) dma_one(tile, v_op, i, phys);
   };
 
-  if (nt > 0) dma_op(0, grp != 0);
+  // Group 0 loads the key tiles, group 1 the value tiles.  Tile 0 flies
+  // while the Q fragments arrive.
+  const bool v_loader = grp != 0;
+  if (nt > 0) dma_op(0, v_loader);
 
   // Scores of one tile: two 32-key blocks, two 64-byte halves of the head dim.
   f32x16 sacc[2];
@@ -258,15 +261,10 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   i32x8 pf;
   bool corr = false;
   float alpha = 1.f;
-  auto weights = [&](float m, float& ps, int dma_tile, bool dma_v, int32_t dma_phys) {
+  auto weights = [&](float m, float& ps) {
     float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      if (dma_tile >= 0 && kc % 2 == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        dma_one(dma_tile, dma_v, kc / 2, dma_phys);
-        __builtin_amdgcn_sched_barrier(0);
-      }
       const int kb = kc >> 1;
       const int r0 = 8 * (kc & 1);
       float pv[8];
@@ -282,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
   };
 
-  auto softmax = [&](int t, int dma_tile, bool dma_v, int32_t dma_phys) {
+  auto softmax = [&](int t) {
     const int k0 = t * kBc;
     const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
     if (need_mask) {
@@ -297,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     // Weights against the current reference; a lane sum above 2^8 (or not
     // finite) sends the wave to the exact step (see the bf16 kernel).
     float ps;
-    weights(m_run, ps, dma_tile, dma_v, dma_phys);
+    weights(m_run, ps);
     corr = __any(!(ps <= kLazyBound));
     if (corr) {
       float mx[4];
@@ -312,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
       alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, -1, false, 0);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps);
     }
     l_run += ps;
   };
@@ -326,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   const int tkey = 8 * (rr >> 3) + 4 * hi + ((rr >> 1) & 3);  // + 16 q
   const int tchunk = gg & 1;                                     // + 2 db
   const int tbyte = 8 * (rr & 1);
-  auto pv = [&](int t) {
+  auto pv = [&](int t, int dma_tile, int32_t dma_phys) {
     if (corr) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -347,18 +345,47 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
       const i32x8 av = {pieces[0][0], pieces[0][1], pieces[1][0], pieces[1][1],
                         pieces[2][0], pieces[2][1], pieces[3][0], pieces[3][1]};
       oacc[db] = mfma_fp8(av, pf, oacc[db]);
+      if (db == 1 && dma_tile >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_one(dma_tile, v_loader, 1, dma_phys);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     lsum = mfma_fp8(ones, pf, lsum);
   };
+  // The MFMA phase of tile t: the scores of tile t + 1 (when it exists), then
+  // P.V of tile t.  When dma_tile >= 0, this wave's two LDS-DMA instructions
+  // for that tile's operand (keys for group 0, values for group 1) go out
+  // between the products, where the matrix pipe hides their issue.
+  auto mfma_phase = [&](int t, int dma_tile, int32_t dma_phys) {
+    if (t + 1 < nt) scores(t + 1);
+    if (dma_tile >= 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma_one(dma_tile, v_loader, 0, dma_phys);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pv(t, dma_tile, dma_phys);
+  };
 
-  // Phase schedule: as in the bf16 prefill (ping-pong of the two groups,
-  // one phase apart; loads from the softmax group; at the end of odd phase
-  // P each wave waits for its share of tile (P+1)/2).
+  // Phase schedule (as in the bf16 prefill): global phases P = 0 .. 2 nt + 1,
+  // each ended by a workgroup barrier.  Group 0 runs the scores of tile 0 in
+  // phase 0, the softmax of tile t in phase 2t + 1 and the MFMA phase of tile
+  // t (scores of t + 1, P.V of t) in phase 2t + 2; group 1 runs the same one
+  // phase later.  So K of tile t is read in phases 2t and 2t + 1, V of tile t
+  // in phases 2t + 2 and 2t + 3.
+  //
+  // Loads into stage t % 4 from the MFMA phases: K of tile t + 3 by group 0
+  // in phase 2t + 2 (K of tile t - 1, in that stage, was last read in phase
+  // 2t - 1), V of tile t + 3 by group 1 in phase 2t + 3 (V of tile t - 1 was
+  // last read in phase 2t + 1).  The prologue loads tiles 0 .. 2 of each
+  // operand.  At the end of odd phase 2s - 1 each wave waits for its share of
+  // tile s (read from phase 2s on); of its later loads, tile s + 1 may still
+  // be in flight.
   auto phase_end = [&](int P) {
     if (P & 1) {
-      const int t_need = (P + 1) / 2;
-      if (t_need < nt) {
-        if (t_need + 1 < nt)
+      const int s_need = (P + 1) / 2;
+      if (s_need < nt) {
+        if (s_need + 1 < nt)
           wait_vmcnt<IPW>();
         else
           wait_vmcnt<0>();
@@ -367,47 +394,49 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     lds_barrier();
   };
   if (nt > 0) {
+    // The Q loads were issued before tile 0's DMA; wait for both, then let
+    // the next tiles fly.
     asm volatile("" : "+v"(qf[0]), "+v"(qf[1]));
     wait_vmcnt<0>();
-    if (nt > 1) dma_op(1, grp != 0);
+    for (int j = 1; j < 3 && j < nt; ++j) dma_op(j, v_loader);
     lds_barrier();
-    // Paged: the table entry for the DMA of the next softmax phase is read
-    // at the end of the MFMA phase before it (as in the bf16 prefill).
+    // Paged: the table entry for the next MFMA phase's DMA is read through
+    // the scalar cache at the start of the softmax phase before it (no LDS
+    // read is pending there: both count on one counter) and waited for at its
+    // end.
+    auto settle = [&](int32_t& e) {
+      if (PAGED) asm volatile("" : "+s"(e));
+    };
     if (grp == 0) {
       scores(0);
-      int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 2 < nt ? t + 2 : -1, true, ph);
+        const int dt = t + 3 < nt ? t + 3 : -1;
+        int32_t ph = pool_block(dt);
+        softmax(t);
+        settle(ph);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < nt) scores(t + 1);
-        pv(t);
+        mfma_phase(t, dt, ph);
         __builtin_amdgcn_s_setprio(0);
-        if (PAGED) {
-          __builtin_amdgcn_sched_barrier(0);
-          ph = pool_block(t + 3 < nt ? t + 3 : -1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
         phase_end(2 * t + 2);
       }
       phase_end(2 * nt + 1);
     } else {
-      if (2 < nt) dma_op(2, false);
-      int32_t ph = pool_block(3 < nt ? 3 : -1);
       phase_end(0);
       scores(0);
       phase_end(1);
       for (int t = 0; t < nt; ++t) {
-        softmax(t, t + 3 < nt ? t + 3 : -1, false, ph);
+        const int dt = t + 3 < nt ? t + 3 : -1;
+        int32_t ph = pool_block(dt);
+        softmax(t);
+        settle(ph);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < nt) scores(t + 1);
-        pv(t);
+        mfma_phase(t, dt, ph);
         __builtin_amdgcn_s_setprio(0);
-        if (PAGED) {
-          __builtin_amdgcn_sched_barrier(0);
-          ph = pool_block(t + 4 < nt ? t + 4 : -1);
-        }
+        __builtin_amdgcn_sched_barrier(0);
         phase_end(2 * t + 3);
       }
     }
