@@ -202,10 +202,11 @@ __device__ __forceinline__ uint4 e4m3x8_bf16x8(uint32_t a, uint32_t b) {
                     e4m3x2_bf16x2<true>(b));
 }
 
-// Waves per SIMD the split kernel is built for: three (168 registers), or
-// one at head_dim 256 (its ring, accumulator and Q fragments need more than
-// 256 registers; the rest goes to the accumulation registers), or four with
-// E4M3 pools (128 registers).  A few values spill at three and four.
+// Waves per SIMD the split kernel is built for: three (at most 168
+// registers; head_dim 128 takes 164), or one at head_dim 256 (its ring,
+// accumulator and Q fragments need more than 256 registers; the rest goes to
+// the accumulation registers), or four with E4M3 pools (128 registers: the
+// two 64-bit row pointers used only at piece boundaries spill).
 template <int D, bool KV8 = false>
 constexpr int split_waves_per_simd() { return D == 256 ? 1 : (KV8 ? 4 : 3); }
 
@@ -248,12 +249,12 @@ decode_split_kernel(const DecodeParams p) {
   // block (the host keeps it below 2^31).
   const char* __restrict__ kpool = (const char*)p.k_pool + (int64_t)g * p.p_hs * ES;
   const char* __restrict__ vpool = (const char*)p.v_pool + (int64_t)g * p.p_hs * ES;
-  uint32_t koff[NL], voff[NL];
-#pragma unroll
-  for (int s = 0; s < NL; ++s) {
-    koff[s] = KV8 ? (uint32_t)(n * p.p_ts + 64 * s + 16 * j) : (uint32_t)((n * p.p_ts + 32 * s + 8 * j) * 2);
-    voff[s] = (uint32_t)((s * VTPL + lane / VCHL) * p.p_ts * ES + 16 * (lane % VCHL));
-  }
+  // Load s of a block adds 64 s bytes to the key offset (an immediate) and
+  // s VTPL rows to the value base (a uniform step), so one per-lane offset
+  // per operand serves every load.
+  const uint32_t koff = KV8 ? (uint32_t)(n * p.p_ts + 16 * j) : (uint32_t)((n * p.p_ts + 8 * j) * 2);
+  const uint32_t voff = (uint32_t)((lane / VCHL) * p.p_ts * ES + 16 * (lane % VCHL));
+  const int64_t vstep = (int64_t)VTPL * p.p_ts * ES;
 
   // Q of head n as the B operand of the score product (zero for columns
   // past the group).
@@ -286,9 +287,9 @@ decode_split_kernel(const DecodeParams p) {
       const char* kb = kpool + base;
       const char* vb = vpool + base;
 #pragma unroll
-      for (int s = 0; s < NL; ++s) B.k[s] = load_stream(kb + koff[s]);
+      for (int s = 0; s < NL; ++s) B.k[s] = load_stream(kb + koff + 64 * s);
 #pragma unroll
-      for (int s = 0; s < NL; ++s) B.v[s] = load_stream(vb + voff[s]);
+      for (int s = 0; s < NL; ++s) B.v[s] = load_stream(vb + s * vstep + voff);
       if (++n_issued < n_units) cursor_next(p, ic);
     }
   };
