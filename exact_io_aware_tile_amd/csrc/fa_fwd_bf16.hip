@@ -11,9 +11,10 @@
 //
 // gfx950 mapping
 //   * one workgroup per CU: 8 waves (2 per SIMD) x 32 query rows = 256 rows
-//     of one (sequence, head).  Wave w owns rows q0 + w, q0 + w + 8, ...,
-//     q0 + w + 248, so under a causal mask every wave sees the same number of
-//     key tiles.  Q fragments and the output accumulator stay in registers.
+//     of one (sequence, head).  Wave w owns rows q0 + 32 w .. +31, so under a
+//     causal mask only the waves at the diagonal mask a tile, and the first
+//     four waves (128 rows) stop computing two tiles before the last four.
+//     Q fragments and the output accumulator stay in registers.
 //   * key and value tiles of 64 rows go from global memory straight into LDS
 //     (global_load_lds, 16 bytes per lane, no register staging) through a
 //     ring of 4 stages.  Rows are stored whole (d contiguous) with the 16-byte
@@ -155,21 +156,32 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   o_base += (int64_t)h * p.o_hs;
   const int off = nk - nq;  // causal: key j visible from row i iff j <= i + off
 
-  // Key tiles the workgroup streams (every wave uses all of them).
+  // Key tiles the workgroup streams.  Under a causal mask the first 128 rows
+  // (group 0) see no key of the last tiles: that group computes only its
+  // first nt0 tiles and then keeps to the phase barriers (and its load
+  // waits) while group 1 finishes alone.  nt0 >= nt - 3 holds by
+  // construction, so the keys group 0 loads four tiles ahead are all issued
+  // before it stops.
   int nt = (nk + kBc - 1) / kBc;
+  int nt0 = nt;
   if (CAUSAL) {
     const int last = q0 + kBr - 1 + off;
     const int lim = last < 0 ? 0 : last / kBc + 1;
     nt = nt < lim ? nt : lim;
+    const int last0 = q0 + kBr / 2 - 1 + off;
+    const int lim0 = last0 < 0 ? 0 : last0 / kBc + 1;
+    nt0 = max(min(nt, lim0), max(nt - 3, 1));
   }
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + q_base;
   const uint16_t* __restrict__ kg = (const uint16_t*)p.k + k_base;
   const uint16_t* __restrict__ vg = (const uint16_t*)p.v + v_base;
 
-  // This lane's query row and its Q fragments Q[row][16*kk + 8*hi .. +7].
-  const int row = q0 + 8 * l32 + wave;
-  const int wrow0 = q0 + wave;  // the wave's first row
+  // This lane's query row and its Q fragments Q[row][16*kk + 8*hi .. +7]:
+  // wave w owns rows q0 + 32 w .. +31, so group 0 (waves 0-3) holds the
+  // first 128 rows of the tile and group 1 the last 128.
+  const int row = q0 + 32 * wave + l32;
+  const int wrow0 = q0 + 32 * wave;  // the wave's first row
   // A row past the end of the queries (never stored) reads the last valid
   // row instead: each row's scores, max and sum stay in its own lane.
   bf16x8 qf[D / 16];
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       scores0();
       if (DROP) draw(0);
       phase_end(0);
-      for (int t = 0; t < nt - 1; ++t) {
+      for (int t = 0; t < nt0 - 1; ++t) {
         int32_t ph = table_entry(t + 4 < nt ? t + 4 : -1);
         softmax(t);
         settle(ph);
@@ -572,15 +584,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         phase_end(2 * t + 2);
       }
-      softmax(nt - 1);
-      prefetch(nt - 1);
-      phase_end(2 * nt - 1);
+      softmax(nt0 - 1);
+      prefetch(nt0 - 1);
+      phase_end(2 * nt0 - 1);
       __builtin_amdgcn_s_setprio(1);
-      mfma_phase(nt - 1, last, -1, 0);
+      mfma_phase(nt0 - 1, last, -1, 0);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      phase_end(2 * nt);
-      phase_end(2 * nt + 1);
+      phase_end(2 * nt0);
+      for (int P = 2 * nt0 + 1; P <= 2 * nt + 1; ++P) phase_end(P);
     } else {
       phase_end(0);
       scores0();
@@ -639,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     const int r = s * RPS + lane / CH;
     const int cc = lane % CH;
     const uint4 v = *(const uint4*)&stage[r * D + (cc ^ (r & (CH - 1))) * 8];
-    const int orow = q0 + 8 * r + wave;
+    const int orow = q0 + 32 * wave + r;
     if (orow < nq) *(uint4*)(og + (int64_t)orow * p.o_ss + cc * 8) = v;
   }
   if (row < nq && p.lse && hi == 0)
