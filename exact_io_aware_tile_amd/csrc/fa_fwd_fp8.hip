@@ -9,7 +9,8 @@
 //
 // gfx950 mapping (the bf16 kernel's pipeline, with FP8 operands)
 //   * one workgroup per CU: 8 waves (2 per SIMD) x 32 query rows = 256 rows
-//     of one (sequence, head); wave w owns rows q0 + w, q0 + w + 8, ...
+//     of one (sequence, head); wave w owns rows q0 + 32 w .. +31, and under a
+//     causal mask the first four waves stop two tiles before the last four.
 //   * 64-key tiles of K and V (8 KB each: 64 rows of 128 bytes) go from
 //     global memory straight into LDS (global_load_lds) through a 4-stage
 //     ring, 16-byte chunks XOR-swizzled per row pair so that both the score
@@ -130,11 +131,18 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   o_base += (int64_t)h * p.o_hs;
   const int off = nk - nq;  // causal: key j visible from row i iff j <= i + off
 
+  // Key tiles the workgroup streams; under a causal mask the first 128 rows
+  // (group 0) need only the first nt0 of them (as in the bf16 prefill; nt0 >=
+  // nt - 3, so group 0 has issued every key load by the time it stops).
   int nt = (nk + kBc - 1) / kBc;
+  int nt0 = nt;
   if (CAUSAL) {
     const int last = q0 + kBr - 1 + off;
     const int lim = last < 0 ? 0 : last / kBc + 1;
     nt = nt < lim ? nt : lim;
+    const int last0 = q0 + kBr / 2 - 1 + off;
+    const int lim0 = last0 < 0 ? 0 : last0 / kBc + 1;
+    nt0 = max(min(nt, lim0), max(nt - 3, 1));
   }
 
   const uint8_t* __restrict__ qg = (const uint8_t*)p.q + q_base;
@@ -142,9 +150,10 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   const uint8_t* __restrict__ vg = (const uint8_t*)p.v + v_base;
 
   // This lane's query row and its Q fragments: qf[kk] = Q[row][64 kk + 32 hi
-  // .. +31].  A row past the end (never stored) reads the last valid row.
-  const int row = q0 + 8 * l32 + wave;
-  const int wrow0 = q0 + wave;
+  // .. +31]; wave w owns rows q0 + 32 w .. +31.  A row past the end (never
+  // stored) reads the last valid row.
+  const int row = q0 + 32 * wave + l32;
+  const int wrow0 = q0 + 32 * wave;
   i32x8 qf[2];
   {
     const uint8_t* qr = qg + (int64_t)min(row, nq - 1) * p.q_ss + 32 * hi;
@@ -357,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   // P.V of tile t.  When dma_tile >= 0, this wave's two LDS-DMA instructions
   // for that tile's operand (keys for group 0, values for group 1) go out
   // between the products, where the matrix pipe hides their issue.
-  auto mfma_phase = [&](int t, int dma_tile, int32_t dma_phys) {
-    if (t + 1 < nt) scores(t + 1);
+  auto mfma_phase = [&](int t, int dma_tile, int32_t dma_phys, int ntg) {
+    if (t + 1 < ntg) scores(t + 1);
     if (dma_tile >= 0) {
       __builtin_amdgcn_sched_barrier(0);
       dma_one(dma_tile, v_loader, 0, dma_phys);
@@ -410,19 +419,21 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     if (grp == 0) {
       scores(0);
       phase_end(0);
-      for (int t = 0; t < nt; ++t) {
+      for (int t = 0; t < nt0; ++t) {
         const int dt = t + 3 < nt ? t + 3 : -1;
         int32_t ph = pool_block(dt);
         softmax(t);
         settle(ph);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
-        mfma_phase(t, dt, ph);
+        mfma_phase(t, dt, ph, nt0);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         phase_end(2 * t + 2);
       }
-      phase_end(2 * nt + 1);
+      // past its last tile: the barriers and load waits only, while group 1
+      // finishes alone
+      for (int P = 2 * nt0 + 1; P <= 2 * nt + 1; ++P) phase_end(P);
     } else {
       phase_end(0);
       scores(0);
@@ -434,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
         settle(ph);
         phase_end(2 * t + 2);
         __builtin_amdgcn_s_setprio(1);
-        mfma_phase(t, dt, ph);
+        mfma_phase(t, dt, ph, nt);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         phase_end(2 * t + 3);
@@ -467,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     const int r = s * RPS + lane / OCH;
     const int cc = lane % OCH;
     const uint4 v = *(const uint4*)&stage[r * D + (cc ^ (r & (OCH - 1))) * 8];
-    const int orow = q0 + 8 * r + wave;
+    const int orow = q0 + 32 * wave + r;
     if (orow < nq) *(uint4*)(og + (int64_t)orow * p.o_ss + cc * 8) = v;
   }
   if (row < nq && p.lse && hi == 0)
