@@ -135,21 +135,30 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   o_base += (int64_t)h * p.o_hs;
   const int off = nk - nq;  // causal: key i visible from row r iff i <= r + off
 
+  // Key tiles the workgroup streams; under a causal mask the first 64 rows
+  // (group 0) need only the first nt0 of them and then keep to the barriers
+  // and their load waits while group 1 finishes alone.  Group 0 loads the
+  // values two tiles ahead, so nt0 >= nt - 2 (which the 64-row offset of the
+  // groups gives anyway) keeps every value load issued before it stops.
   int nt = (nk + kBc - 1) / kBc;
+  int nt0 = nt;
   if (CAUSAL) {
     const int last = q0 + kBr - 1 + off;
     const int lim = last < 0 ? 0 : last / kBc + 1;
     nt = nt < lim ? nt : lim;
+    const int last0 = q0 + kBr / 2 - 1 + off;
+    const int lim0 = last0 < 0 ? 0 : last0 / kBc + 1;
+    nt0 = max(min(nt, lim0), max(nt - 2, 1));
   }
 
   const uint16_t* __restrict__ qg = (const uint16_t*)p.q + q_base;
   const uint16_t* __restrict__ kg = (const uint16_t*)p.k + k_base;
   const uint16_t* __restrict__ vg = (const uint16_t*)p.v + v_base;
 
-  // Wave w owns rows q0 + w + 8i (i = 0..15); lane l holds row q0 + w +
-  // 8(l%16).  Rows past the end read the last valid row (never stored).
-  const int row = q0 + 8 * n + wave;
-  const int wrow0 = q0 + wave;
+  // Wave w owns rows q0 + 16 w .. +15; lane l holds row q0 + 16 w + l%16.
+  // Rows past the end read the last valid row (never stored).
+  const int row = q0 + 16 * wave + n;
+  const int wrow0 = q0 + 16 * wave;
   bf16x8 qf[D / 32];  // Q[row][32s + 8j .. +7]
   {
     const uint16_t* qr = qg + (int64_t)min(row, nq - 1) * p.q_ss + 8 * j;
@@ -419,18 +428,18 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
       scores(0);
       int32_t ph = pool_block(2 < nt ? 2 : -1);
       phase_end(0);
-      for (int t = 0; t < nt; ++t) {
+      for (int t = 0; t < nt0; ++t) {
         softmax(t, t + 2 < nt ? t + 2 : -1, true, ph);
         phase_end(2 * t + 1);
         __builtin_amdgcn_s_setprio(1);
-        if (t + 1 < nt) scores(t + 1);
+        if (t + 1 < nt0) scores(t + 1);
         pv(t);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         ph = pool_block(t + 3 < nt ? t + 3 : -1);
         phase_end(2 * t + 2);
       }
-      phase_end(2 * nt + 1);
+      for (int P = 2 * nt0 + 1; P <= 2 * nt + 1; ++P) phase_end(P);
     } else {
       if (2 < nt) dma_op(2, false);
       int32_t ph = pool_block(3 < nt ? 3 : -1);
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     const int r = s * RPS + lane / CH;
     const int cc = lane % CH;
     const uint4 v = *(const uint4*)&stage[r * D + (cc ^ r) * 8];
-    const int orow = q0 + 8 * r + wave;
+    const int orow = q0 + 16 * wave + r;
     if (orow < nq) *(uint4*)(og + (int64_t)orow * p.o_ss + cc * 8) = v;
   }
   if (row < nq && p.lse && j == 0)
