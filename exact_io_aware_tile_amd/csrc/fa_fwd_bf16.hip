@@ -593,6 +593,18 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
       phase_end(2 * nt0);
       for (int P = 2 * nt0 + 1; P <= 2 * nt + 1; ++P) phase_end(P);
+    } else if (q0 + kBr / 2 >= nq) {
+      // No row of group 1 exists in this tile (the last, ragged tile of a
+      // sequence): it only loads its value tiles, three ahead in what would
+      // be its MFMA phases, and keeps to the barriers and its load waits
+      // while group 0 computes alone.
+      phase_end(0);
+      phase_end(1);
+      for (int t = 0; t < nt; ++t) {
+        phase_end(2 * t + 2);
+        if (t + 3 < nt) dma_op(t + 3, true);
+        phase_end(2 * t + 3);
+      }
     } else {
       phase_end(0);
       scores0();
