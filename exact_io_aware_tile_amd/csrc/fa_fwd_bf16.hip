@@ -79,6 +79,8 @@ constexpr float kLazyBound = 65536.f;  // largest weight (2^16) formed against a
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 // LDS swizzles, for 64 banks of 4 bytes.  ch = 16-byte chunks per row (16 or 8).
 // Physical chunk of logical chunk c in key row r: the score-operand reads
@@ -429,27 +431,52 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // Value reads: the swizzle of key rows 16 kc + 4 hi + tk (+ 8) depends on
   // tk only, so each 32-dim block db has one per-lane LDS address for stage
   // 0; chunk kc, the upper 8 keys and the stage add uniform offsets.
-  uint32_t vbase[D / 32];
+  uint32_t vbt[D / 32];  // value reads of the current tile's stage
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int dc = 4 * db + 2 * (g16 & 1) + (tq >> 1);  // logical 16-byte chunk
     const int ka = 4 * hi + tk;
-    vbase[db] = (uint32_t)(uintptr_t)&v_s[0][0] + 2u * (uint32_t)(ka * D + swz_v(CH, ka, dc) * 8 + 4 * (tq & 1));
+    vbt[db] = (uint32_t)(uintptr_t)&v_s[0][0] + 2u * (uint32_t)(ka * D + swz_v(CH, ka, dc) * 8 + 4 * (tq & 1));
   }
+  // Key reads: key row l32 (+32 for the second block, an immediate: the
+  // swizzle of row r depends on r mod 32 only), chunk 2kk + hi.
+  uint32_t kbt[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    kbt[kk] = (uint32_t)(uintptr_t)&k_s[0][0] + 2u * (uint32_t)(l32 * D + swz_k(CH, l32, 2 * kk + hi) * 8);
+  // The per-lane bases follow the ring one stage per tile: tile j lives in
+  // stage j % kStages.  Each wave moves its value bases once per tile (in the
+  // prefetch) and its key bases once per tile read (in the MFMA phase), in
+  // tile order, so a read adds only an immediate.
+  auto stage_step = [&](int j) {  // byte step from the stage of tile j - 1 to that of tile j
+    return (j % kStages == 0) ? (uint32_t)(-(int)(2 * (kStages - 1) * TILE)) : (uint32_t)(2 * TILE);
+  };
+  auto advance_v = [&](int t) {
+    if (t > 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) vbt[db] += stage_step(t);
+    }
+  };
+  auto advance_k = [&](int j) {
+    if (j > 0) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) kbt[kk] += stage_step(j);
+    }
+  };
   auto read_op = [&](int i, int t) {
     if (i < NPV) {
       const int kc = i / (D / 32), db = i % (D / 32);
-      const uint32_t a = vbase[db] + 2u * (uint32_t)((t % kStages) * TILE) + 2u * (uint32_t)(16 * kc * D);
+      const uint32_t a = vbt[db] + 2u * (uint32_t)(16 * kc * D);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a);
       const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(a + 2u * 8u * D));
       const uint2 l2 = __builtin_bit_cast(uint2, lo);
       const uint2 u2 = __builtin_bit_cast(uint2, up);
       opa[i] = make_uint4(l2.x, l2.y, u2.x, u2.y);
     } else {
-      const uint16_t* ks = &k_s[(t + 1) % kStages][0];
       const int kk = (i - NPV) >> 1, kb = (i - NPV) & 1;
-      const int r = kb * 32 + l32;
-      opa[i] = *(const uint4*)&ks[r * D + swz_k(CH, r, 2 * kk + hi) * 8];
+      const uint32_t a = kbt[kk] + 2u * (uint32_t)(kb * 32 * D);
+      const u32x4_t v = *(const lds_u32x4*)(uintptr_t)a;
+      opa[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
   auto mfma_op = [&](int i) {
@@ -464,6 +491,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // Reads of the first kPre products of tile t's phase, at the end of the
   // softmax phase before it (only the value tile, already visible, is read).
   auto prefetch = [&](int t) {
+    advance_v(t);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kPre; ++i) read_op(i, t);
@@ -478,6 +506,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   auto mfma_phase = [&](int t, auto next, int dma_tile, int32_t dma_phys) {
     constexpr int N = decltype(next)::value ? NPV + NSC : NPV;
     constexpr int DSTEP = N / IPW;
+    if (decltype(next)::value) advance_k(t + 1);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       mfma_op(i);
