@@ -61,6 +61,8 @@ static_assert(IPW == 4 && RPW % RPI == 0, "DMA split");
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 __device__ __forceinline__ f32x4 zero4() {
   f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -245,18 +247,36 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
 
   if (nt > 0) dma_op(0, grp != 0);
 
+  // Per-lane LDS operand addresses in stage 0, moved one stage per tile
+  // (tile j lives in stage j % kStages) by the wave that reads them, in tile
+  // order, so each read adds only an immediate.  Keys: row n (+16 rows for
+  // the second block), chunk 4s + j; the swizzle leaves bit 4 of the chunk,
+  // so s and s + 4 differ by 16 chunks.  Values: rows 4j + tk (+16 rows),
+  // chunk 2db + (tq >> 1), db and db + 8 likewise 16 chunks apart.
+  uint32_t kaddr[4], vaddr[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    kaddr[s] = (uint32_t)(uintptr_t)&k_s[0][0] + 2u * (uint32_t)(n * D + swz_k(n, 4 * s + j) * 8);
+  auto stage_step = [&](int t) {  // bytes from the stage of tile t - 1 to that of tile t
+    return (t % kStages == 0) ? (uint32_t)(-(int)(2 * (kStages - 1) * TILE)) : (uint32_t)(2 * TILE);
+  };
+
   // Scores of one tile: two 16-key blocks, sacc[kb][r] = S[key 16kb + 4j + r][row].
   f32x4 sacc[2];
   auto scores = [&](int t) {
-    const uint16_t* ks = &k_s[t % kStages][0];
+    if (t > 0) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kaddr[s] += stage_step(t);
+    }
     sacc[0] = zero4();
     sacc[1] = zero4();
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int r = 16 * kb + n;
-        const uint4 a = *(const uint4*)&ks[r * D + swz_k(r, 4 * s + j) * 8];
+        const uint32_t ad = kaddr[s & 3] + 2u * (uint32_t)(16 * (s >> 2) * 8 + 16 * kb * D);
+        const u32x4_t av = *(const lds_u32x4*)(uintptr_t)ad;
+        const uint4 a = make_uint4(av.x, av.y, av.z, av.w);
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[s], sacc[kb], 0, 0,
                                                            0);
       }
@@ -364,26 +384,31 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
   // read leaves lane n with dim 16db + n of four keys of its block.
   const int tk = n >> 2;
   const int tq = n & 3;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const int va = 4 * j + tk;
+    vaddr[d] = (uint32_t)(uintptr_t)&v_s[0][0] +
+               2u * (uint32_t)(va * D + swz_v(va, 2 * d + (tq >> 1)) * 8 + 4 * (tq & 1));
+  }
   auto pv = [&](int t) {
+    if (t > 0) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) vaddr[d] += stage_step(t);
+    }
     if (corr) {
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
 #pragma unroll
         for (int r = 0; r < 4; ++r) oacc[db][r] *= alpha;
     }
-    const uint16_t* vs = &v_s[t % kStages][0];
     const uint2 p0 = __builtin_bit_cast(uint2, pf[0]);
     const uint2 p1 = __builtin_bit_cast(uint2, pf[1]);
     const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(p0.x, p0.y, p1.x, p1.y));
-    const int va = 4 * j + tk;
-    const int vb = 16 + 4 * j + tk;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const int dc = 2 * db + (tq >> 1);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&vs[va * D + swz_v(va, dc) * 8 + 4 * (tq & 1)]);
-      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&vs[vb * D + swz_v(vb, dc) * 8 + 4 * (tq & 1)]);
+      const uint32_t ad = vaddr[db & 7] + 2u * (uint32_t)(16 * (db >> 3) * 8);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)ad);
+      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(ad + 2u * 16u * D));
       const uint2 l2 = __builtin_bit_cast(uint2, lo);
       const uint2 u2 = __builtin_bit_cast(uint2, up);
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
