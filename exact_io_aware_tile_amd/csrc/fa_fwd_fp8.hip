@@ -53,6 +53,8 @@ constexpr uint32_t kOnesE4M3 = 0x38383838u;  // four E4M3 1.0
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 // D(32x32 fp32) += A(32x64 E4M3) * B(64x32 E4M3), unit block scales.
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -211,25 +213,23 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
     const int rows_left = nk - tile * kBc;  // uniform
-    uint32_t o = v_op ? voff[i] : koff[i];
-    if (PAGED) {
-      if (rows_left < kBc) {
-        const int r = r0 + drow;
-        const int key = tile * kBc + min(r, rows_left - 1);
-        const int rb = key - wave_block(tile) * kFwdPagedBlock;
-        o = (uint32_t)((int64_t)rb * p.p_ts + swz(r, dpch) * 16);
-      }
-      dma_16b((v_op ? vg : kg) + (int64_t)phys * p.p_bs, o, lds);
+    const uint8_t* base = PAGED ? (v_op ? vg : kg) + (int64_t)phys * p.p_bs
+                                : (v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss);
+    // A full tile takes the precomputed offsets as they are (each branch
+    // issues its own load, so no offset is copied in the common case); in
+    // the last tile rows past the last key re-read that key (in the last
+    // key's block when paged).
+    if (rows_left >= kBc) {
+      dma_16b(base, v_op ? voff[i] : koff[i], lds);
     } else {
-      const uint8_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
-      if (rows_left < kBc) {
-        const int r = r0 + drow;
-        const int rk = min(r, rows_left - 1);
-        o = (uint32_t)((int64_t)rk * (v_op ? p.v_ss : p.k_ss) + swz(r, dpch) * 16);
-      }
-      dma_16b(base, o, lds);
+      const int r = r0 + drow;
+      const int64_t row_stride = PAGED ? p.p_ts : (v_op ? p.v_ss : p.k_ss);
+      const int rk = PAGED ? tile * kBc + min(r, rows_left - 1) - wave_block(tile) * kFwdPagedBlock
+                           : min(r, rows_left - 1);
+      dma_16b(base, (uint32_t)((int64_t)rk * row_stride + swz(r, dpch) * 16), lds);
     }
   };
+
   auto dma_op = [&](int tile, bool v_op) {
     const int32_t phys = pool_block(tile);
 #pragma unroll
@@ -243,16 +243,38 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
 
   // Scores of one tile: two 32-key blocks, two 64-byte halves of the head dim.
   f32x16 sacc[2];
+  // Per-lane LDS operand addresses in stage 0, moved one stage per tile
+  // (tile j lives in stage j % kStages) by the wave that reads them, in tile
+  // order, so each read adds only an immediate.  Keys: row l32 (+32 rows
+  // for the second block: the swizzle of row r depends on r mod 32 only),
+  // chunk 4kk + 2hi + u.  Values: key rows tkey (+16 q rows), chunk
+  // 2db + tchunk.
+  uint32_t kaddr[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      kaddr[kk][u] = (uint32_t)(uintptr_t)&k_s[0][0] + (uint32_t)(l32 * D + swz(l32, 4 * kk + 2 * hi + u) * 16);
+  auto stage_step = [&](int t) {  // bytes from the stage of tile t - 1 to that of tile t
+    return (t % kStages == 0) ? (uint32_t)(-(int)((kStages - 1) * TILE)) : (uint32_t)TILE;
+  };
   auto scores = [&](int t) {
-    const uint8_t* ks = &k_s[t % kStages][0];
+    if (t > 0) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) kaddr[kk][u] += stage_step(t);
+    }
     uint4 a[2][2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + l32;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) a[kk][kb][u] = *(const uint4*)&ks[r * D + swz(r, 4 * kk + 2 * hi + u) * 16];
+        for (int u = 0; u < 2; ++u) {
+          const u32x4_t v = *(const lds_u32x4*)(uintptr_t)(kaddr[kk][u] + (uint32_t)(32 * kb * D));
+          a[kk][kb][u] = make_uint4(v.x, v.y, v.z, v.w);
+        }
       }
     sacc[0] = zero16();
     sacc[1] = zero16();
@@ -333,7 +355,15 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
   const int tkey = 8 * (rr >> 3) + 4 * hi + ((rr >> 1) & 3);  // + 16 q
   const int tchunk = gg & 1;                                     // + 2 db
   const int tbyte = 8 * (rr & 1);
+  uint32_t vaddr[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+    vaddr[db] = (uint32_t)(uintptr_t)&v_s[0][0] + (uint32_t)(tkey * D + swz(tkey, 2 * db + tchunk) * 16 + tbyte);
   auto pv = [&](int t, int dma_tile, int32_t dma_phys) {
+    if (t > 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) vaddr[db] += stage_step(t);
+    }
     if (corr) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -341,16 +371,12 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       lsum[0] *= alpha;  // the only register of lsum that is read
     }
-    const uint8_t* vs = &v_s[t % kStages][0];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       i32x2 pieces[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int key = 16 * q + tkey;
-        pieces[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i32x2*)&vs[key * D + swz(key, 2 * db + tchunk) * 16 + tbyte]);
-      }
+      for (int q = 0; q < 4; ++q)
+        pieces[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(vaddr[db] + (uint32_t)(16 * q * D)));
       const i32x8 av = {pieces[0][0], pieces[0][1], pieces[1][0], pieces[1][1],
                         pieces[2][0], pieces[2][1], pieces[3][0], pieces[3][1]};
       oacc[db] = mfma_fp8(av, pf, oacc[db]);
