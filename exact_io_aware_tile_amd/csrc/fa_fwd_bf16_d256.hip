@@ -215,30 +215,23 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_d256_kernel(const FwdParams
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
     const int rows_left = nk - tile * kBc;  // uniform
-    uint32_t o = v_op ? voff[i] : koff[i];
-    if (PAGED) {
-      // In the last tile rows past the last key re-read that key, in the
-      // last key's block.
-      if (rows_left < kBc) {
-        const int r = r0 + drow;
-        const int key = tile * kBc + min(r, rows_left - 1);
-        const int rb = key - wave_block(tile) * kFwdPagedBlock;
-        o = v_op ? (uint32_t)(((int64_t)rb * p.p_ts + swz_v(r, dpch) * 8) * 2)
-                 : (uint32_t)(((int64_t)rb * p.p_ts + swz_k(r, dpch) * 8) * 2);
-      }
-      const uint16_t* base = (v_op ? vg : kg) + (int64_t)phys * p.p_bs;
-      dma_16b(base, o, lds);
+    const uint16_t* base = PAGED ? (v_op ? vg : kg) + (int64_t)phys * p.p_bs
+                                 : (v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss);
+    // A full tile takes the precomputed offsets as they are (each branch
+    // issues its own load, so no offset is copied in the common case); in
+    // the last tile rows past the last key re-read that key (in the last
+    // key's block when paged).
+    if (rows_left >= kBc) {
+      dma_16b(base, v_op ? voff[i] : koff[i], lds);
     } else {
-      const uint16_t* base = v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss;
-      if (rows_left < kBc) {
-        const int r = r0 + drow;
-        const int rk = min(r, rows_left - 1);
-        o = v_op ? (uint32_t)(((int64_t)rk * p.v_ss + swz_v(r, dpch) * 8) * 2)
-                 : (uint32_t)(((int64_t)rk * p.k_ss + swz_k(r, dpch) * 8) * 2);
-      }
-      dma_16b(base, o, lds);
+      const int r = r0 + drow;
+      const int64_t row_stride = PAGED ? p.p_ts : (v_op ? p.v_ss : p.k_ss);
+      const int rk = PAGED ? tile * kBc + min(r, rows_left - 1) - wave_block(tile) * kFwdPagedBlock
+                           : min(r, rows_left - 1);
+      dma_16b(base, (uint32_t)(((int64_t)rk * row_stride + (v_op ? swz_v(r, dpch) : swz_k(r, dpch)) * 8) * 2), lds);
     }
   };
+
   auto dma_op = [&](int tile, bool v_op) {
     const int32_t phys = pool_block(tile);
 #pragma unroll
