@@ -199,7 +199,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   const uint64_t rid = (uint64_t)(lse_base + row);
   float m_run = -INFINITY;  // base-2 reference max of this lane's row
   float l_run = 0.f;        // this half-wave's share of the running fp32 sum of weights (LSE)
-  float lb_run = 0.f;       // ... of the bf16-rounded weights P.V takes (normalises o)
+  // ... of the bf16-rounded weights P.V takes (normalises o), as four running
+  // partial sums that each tile's v_dot2 chains extend in place.
+  float lb4[4] = {0.f, 0.f, 0.f, 0.f};
   const float c = p.scale_log2;
 
   // DMA of one operand (K or V) of one tile into its LDS stage by the four
@@ -295,12 +297,13 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // of the MFMA phase before it).
   // Weights p = 2^(s*c - m) of the tile for reference m: packed into the
   // bf16 B operands pf of the P.V product; this lane's sum of the fp32
-  // weights goes to ps, and of the rounded ones (v_dot2 with (1, 1) on the
-  // packed pairs, before any dropout) to pb.
+  // weights goes to ps, and the rounded ones (v_dot2 with (1, 1) on the
+  // packed pairs, before any dropout) extend the running sums lb4 into pb4.
   const bf16x2 ones2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-  auto weights = [&](float m, float& ps, float& pb) {
-    float ps4[4] = {0.f, 0.f, 0.f, 0.f};
-    float pb4[4] = {0.f, 0.f, 0.f, 0.f};
+  auto weights = [&](float m, float& ps, float (&pb4)[4]) {
+    float ps4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pb4[q] = lb4[q];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int kb = kc >> 1;
@@ -309,7 +312,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         pv[j] = exp2_fast(__builtin_fmaf(sacc[kb][r0 + j], c, -m));
-        ps4[j & 3] += pv[j];
+        if (kc == 0 && j < 4)
+          ps4[j] = pv[j];
+        else
+          ps4[j & 3] += pv[j];
       }
       uint4 pw;
       pw.x = pack_bf16x2(pv[0], pv[1]);
@@ -330,7 +336,6 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       pf[kc] = __builtin_bit_cast(bf16x8, pw);
     }
     ps = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
-    pb = (pb4[0] + pb4[1]) + (pb4[2] + pb4[3]);
   };
 
   // Dropout bytes of tile t into dw.  Both halves of the wave hold the same
@@ -375,8 +380,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     // sum (a large jump of the max, or no reference yet) sends the whole wave
     // to the exact step, which takes the row max, moves the reference and
     // recomputes the weights.
-    float ps, pb;
-    weights(m_run, ps, pb);
+    float ps, pb4[4];
+    weights(m_run, ps, pb4);
     if (__any(!(ps <= kLazyBound))) {
       float mx[4];
 #pragma unroll
@@ -389,16 +394,18 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       l_run *= alpha;
-      lb_run *= alpha;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lb4[q] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
-      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb);
+      weights(m_new == -INFINITY ? 0.f : m_new, ps, pb4);
     }
     l_run += ps;
-    lb_run += pb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lb4[q] = pb4[q];
   };
 
   // The MFMA phase of tile t is one stream of products: the NPV products
@@ -664,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // a dominant weight, up to 2^-9 relative, into O); LSE = (m + log2 l) *
   // ln 2 with the fp32 sum l.
   const float l_tot = sum_halves(l_run);
-  const float lb_tot = sum_halves(lb_run);
+  const float lb_tot = sum_halves((lb4[0] + lb4[1]) + (lb4[2] + lb4[3]));
   const float inv = (lb_tot > 0.f ? 1.f / lb_tot : 0.f) * (DROP ? p.drop_scale : 1.f);
   // The wave's 32 output rows go through LDS (the tile ring is idle: every
   // tile has been consumed behind the last barrier) so that global stores
