@@ -15,9 +15,9 @@
 //     causal mask only the waves at the diagonal mask a tile, and the first
 //     four waves (128 rows) stop computing two tiles before the last four.
 //     Q fragments and the output accumulator stay in registers.
-//   * key and value tiles of 64 rows go from global memory straight into LDS
-//     (global_load_lds, 16 bytes per lane, no register staging) through a
-//     ring of 4 stages.  Rows are stored whole (d contiguous) with the 16-byte
+//   * key and value tiles of 64 rows (128 in the dense and packed head-dim-64
+//     instances) go from global memory straight into LDS (global_load_lds,
+//     16 bytes per lane, no register staging) through a ring of 4 stages.  Rows are stored whole (d contiguous) with the 16-byte
 //     chunks of each row XOR-swizzled so that both the score-operand reads and
 //     the transposed value reads hit distinct banks.  The waves in their
 //     MFMA phase issue the loads, spread between the products: a load that
@@ -72,7 +72,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 static_assert(kBr == kFwdRowsPerTileBf16, "host tiling must match");
-constexpr int kBc = 64;            // keys per tile
+constexpr int kBc = 64;            // keys per tile (128 in the plain head-dim-64 instance, see BC below)
 constexpr int kStages = 4;         // LDS ring depth
 constexpr float kLazyBound = 65536.f;  // largest weight (2^16) formed against a stale reference
 
@@ -97,10 +97,18 @@ __device__ __forceinline__ int swz_v(int ch, int r, int c) {
 template <int D, bool CAUSAL, bool PAGED, bool DROP>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   static_assert(!(PAGED && DROP), "dropout is built for dense and packed prefill");
+  // Keys per tile: at head_dim 64 a 64-key tile holds only 16 products per
+  // wave and phase against the same per-tile softmax bookkeeping, so the
+  // dense and packed instances take 128 keys (the same 16 KB per stage as
+  // d = 128).  The paged instance keeps 64 (one 16-token pool block per wave
+  // and tile), and so does dropout (128 keys would spill its registers).
+  constexpr int BC = (D == 64 && !PAGED && !DROP) ? 128 : kBc;
+  constexpr int NKB = BC / 32;             // 32-key score blocks of a tile
+  constexpr int NKC = BC / 16;             // 16-key chunks of the P.V contraction
   constexpr int CH = D / 8;                // 16-byte chunks per row
-  constexpr int TILE = kBc * D;            // elements per K or V tile
+  constexpr int TILE = BC * D;             // elements per K or V tile
   constexpr int RPI = 512 / D;              // rows per 1 KB DMA instruction
-  constexpr int RPW = kBc / 4;              // rows per wave when one group loads an operand
+  constexpr int RPW = BC / 4;               // rows per wave when one group loads an operand
   constexpr int IPW = RPW / RPI;            // DMA instructions per wave per operand of a tile
   static_assert(IPW >= 1 && IPW <= 4 && RPW % RPI == 0, "DMA split");
   __shared__ __attribute__((aligned(1024))) uint16_t k_s[kStages][TILE];
@@ -164,14 +172,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // waits) while group 1 finishes alone.  nt0 >= nt - 3 holds by
   // construction, so the keys group 0 loads four tiles ahead are all issued
   // before it stops.
-  int nt = (nk + kBc - 1) / kBc;
+  int nt = (nk + BC - 1) / BC;
   int nt0 = nt;
   if (CAUSAL) {
     const int last = q0 + kBr - 1 + off;
-    const int lim = last < 0 ? 0 : last / kBc + 1;
+    const int lim = last < 0 ? 0 : last / BC + 1;
     nt = nt < lim ? nt : lim;
     const int last0 = q0 + kBr / 2 - 1 + off;
-    const int lim0 = last0 < 0 ? 0 : last0 / kBc + 1;
+    const int lim0 = last0 < 0 ? 0 : last0 / BC + 1;
     nt0 = max(min(nt, lim0), max(nt - 3, 1));
   }
 
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // Paged: the wave's block of tile `tile` (a block past the last key is
   // replaced by the last key's block).
   auto wave_block = [&](int tile) {
-    return __builtin_amdgcn_readfirstlane(min(tile * (kBc / kFwdPagedBlock) + wq, (nk - 1) / kFwdPagedBlock));
+    return __builtin_amdgcn_readfirstlane(min(tile * (BC / kFwdPagedBlock) + wq, (nk - 1) / kFwdPagedBlock));
   };
   // Its pool block, read from the table through the scalar cache (the table
   // is constant during the launch; a vector load would be counted with the
@@ -251,19 +259,19 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
     const int r0 = wq * RPW + i * RPI;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((v_op ? &v_s[st][0] : &k_s[st][0]) + r0 * D));
-    const int rows_left = nk - tile * kBc;  // uniform
+    const int rows_left = nk - tile * BC;  // uniform
     const uint16_t* base = PAGED ? (v_op ? vg : kg) + (int64_t)phys * p.p_bs
-                                 : (v_op ? vg + (int64_t)tile * kBc * p.v_ss : kg + (int64_t)tile * kBc * p.k_ss);
+                                 : (v_op ? vg + (int64_t)tile * BC * p.v_ss : kg + (int64_t)tile * BC * p.k_ss);
     // A full tile takes the precomputed offsets as they are (the load of
     // each branch is issued there, so no offset is copied in the common
     // case).  In the last tile rows past the last key re-read that key (in
     // the last key's block when paged).
-    if (rows_left >= kBc) {
+    if (rows_left >= BC) {
       dma_16b(base, v_op ? voff[i] : koff[i], lds);
     } else {
       const int r = r0 + drow;
       const int64_t row_stride = PAGED ? p.p_ts : (v_op ? p.v_ss : p.k_ss);
-      const int rk = PAGED ? tile * kBc + min(r, rows_left - 1) - wave_block(tile) * kFwdPagedBlock
+      const int rk = PAGED ? tile * BC + min(r, rows_left - 1) - wave_block(tile) * kFwdPagedBlock
                            : min(r, rows_left - 1);
       const uint32_t off = (uint32_t)(((int64_t)rk * row_stride +
                                        (v_op ? swz_v(CH, r, dpch) : swz_k(CH, r, dpch)) * 8) * 2);
@@ -282,15 +290,15 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   const bool v_loader = grp != 0;
   if (nt > 0) dma_op(0, v_loader);
 
-  f32x16 sacc[2];  // S^T of one tile: two 32-key blocks
+  f32x16 sacc[NKB];  // S^T of one tile: NKB 32-key blocks
 
   // Softmax of tile t in place (scores -> weights), producing the bf16 B
   // operands of the P.V product.
-  bf16x8 pf[4];
+  bf16x8 pf[NKC];
   // Dropout bytes of the tile: dw[kc][0] holds the bytes of keys 16kc + 4hi
   // + 0..3 of this lane's row, dw[kc][1] those of keys 16kc + 8 + 4hi + 0..3
   // (words hi and 2 + hi of the generator's output for the 16-key group kc).
-  uint32_t dw[4][2];
+  uint32_t dw[NKC][2];
   const uint32_t tm1 = DROP ? (uint32_t)(p.drop_t - 1) * 0x00010001u : 0u;
   // When a softmax moves the reference, o and l are rescaled by alpha right
   // there, in the vector-ALU phase (o was last written by the P.V products
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) pb4[q] = lb4[q];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       const int kb = kc >> 1;
       const int r0 = 8 * (kc & 1);
       float pv[8];
@@ -346,9 +354,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // the vector ALU is otherwise idle, and the softmax only applies it.
   auto draw = [&](int t) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NKC / 2; ++u) {
       const uint4 r = philox4x32_10(
-          make_uint4((uint32_t)(4 * t + 2 * u + hi), (uint32_t)rid, (uint32_t)(rid >> 32), p.drop_offset),
+          make_uint4((uint32_t)(NKC * t + 2 * u + hi), (uint32_t)rid, (uint32_t)(rid >> 32), p.drop_offset),
           p.drop_seed_lo, p.drop_seed_hi);
       const auto w01 = __builtin_amdgcn_permlane32_swap(r.x, r.y, false, false);
       const auto w23 = __builtin_amdgcn_permlane32_swap(r.z, r.w, false, false);
@@ -360,14 +368,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   };
 
   auto softmax = [&](int t) {
-    const int k0 = t * kBc;
-    const bool need_mask = (k0 + kBc > nk) || (CAUSAL && k0 + kBc - 1 > wrow0 + off);
+    const int k0 = t * BC;
+    const bool need_mask = (k0 + BC > nk) || (CAUSAL && k0 + BC - 1 > wrow0 + off);
     if (need_mask) {
       const int lim = CAUSAL ? row + off : nk - 1;
       const int kend = (nk - 1 < lim ? nk - 1 : lim) - k0 - 4 * hi;
       // One compare and one select per score (a key past kend is masked).
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = sacc[kb][r];
@@ -390,6 +398,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int r = 2; r < 8; ++r) mx[q] = fmaxf(mx[q], sacc[q >> 1][8 * (q & 1) + r]);
       }
+#pragma unroll
+      for (int q = 4; q < NKC; ++q)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) mx[q & 3] = fmaxf(mx[q & 3], sacc[q >> 1][8 * (q & 1) + r]);
       const float tmax = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * c;
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
@@ -423,8 +435,8 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   // of each 16-lane group points at key row (base + k), dims
   // (16-block + 4q .. +3).  Score product j = 2 kk + kb reads key rows
   // 32 kb + l%32, head dims 16 kk + 8 hi .. +7 of tile t + 1.
-  constexpr int NPV = 4 * (D / 32);
-  constexpr int NSC = 2 * (D / 16);
+  constexpr int NPV = NKC * (D / 32);
+  constexpr int NSC = NKB * (D / 16);
   constexpr int kPre = 6;  // products whose operand reads are in flight ahead
   const int g16 = lane >> 4;
   const int tk = (lane >> 2) & 3;
@@ -475,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       const uint2 u2 = __builtin_bit_cast(uint2, up);
       opa[i] = make_uint4(l2.x, l2.y, u2.x, u2.y);
     } else {
-      const int kk = (i - NPV) >> 1, kb = (i - NPV) & 1;
+      const int kk = (i - NPV) / NKB, kb = (i - NPV) % NKB;
       const uint32_t a = kbt[kk] + 2u * (uint32_t)(kb * 32 * D);
       const u32x4_t v = *(const lds_u32x4*)(uintptr_t)a;
       opa[i] = make_uint4(v.x, v.y, v.z, v.w);
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
       const int kc = i / (D / 32), db = i % (D / 32);
       oacc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, opa[i]), pf[kc], oacc[db]);
     } else {
-      const int kk = (i - NPV) >> 1, kb = (i - NPV) & 1;
+      const int kk = (i - NPV) / NKB, kb = (i - NPV) % NKB;
       sacc[kb] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, opa[i]), qf[kk], kk == 0 ? zero16() : sacc[kb]);
     }
   };

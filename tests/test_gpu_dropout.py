@@ -146,7 +146,13 @@ def test_dense_dropout_parity(gpu, shape, causal, p):
     s = 256.0 / (256 - oracle.dropout_threshold(p))
     check(host(o).transpose(0, 2, 1, 3), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, s,
           f"{shape} causal={causal} p={p}")
-    assert torch.equal(lse, lse_plain), "LSE must not depend on dropout"
+    if d == 64:
+        # At head dim 64 the plain kernel takes 128-key tiles and the dropout
+        # kernel 64-key ones, so the running max moves at different points:
+        # the two LSEs agree to fp32 rounding of the sums, not bit for bit.
+        assert torch.allclose(lse, lse_plain, rtol=0, atol=2e-6), "LSE must not depend on dropout"
+    else:
+        assert torch.equal(lse, lse_plain), "LSE must not depend on dropout"
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
