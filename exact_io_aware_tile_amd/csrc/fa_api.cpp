@@ -170,6 +170,7 @@ fa_status fwd_dense(const fa_fwd_args* a, const fa_dropout_args* drop, const cha
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
   p.wi_chunk = wi_chunk(a->seqlen_k, a->head_dim, a->dtype == FA_BF16 ? 2 : 4, p.group);
+  fa::set_work_map(p);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = scale_log2(a->scale);
   hipStream_t s = (hipStream_t)stream;
@@ -232,6 +233,7 @@ fa_status fwd_varlen(const fa_fwd_varlen_args* a, const fa_dropout_args* drop, c
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
   p.wi_chunk = wi_chunk(a->max_seqlen, a->head_dim, a->dtype == FA_BF16 ? 2 : 4, p.group);
+  fa::set_work_map(p);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = scale_log2(a->scale);
   hipStream_t s = (hipStream_t)stream;
@@ -306,6 +308,7 @@ FA_EXPORT fa_status fa_fwd_fp8(const fa_fwd_fp8_args* a, void* stream) {
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
   p.wi_chunk = wi_chunk(a->seqlen_k, a->head_dim, 1, p.group);
+  fa::set_work_map(p);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = (float)((double)a->scale * a->q_descale * a->k_descale * 1.4426950408889634073599);
   p.o_scale = a->v_descale;
@@ -362,6 +365,7 @@ FA_EXPORT fa_status fa_fwd_varlen_fp8(const fa_fwd_varlen_fp8_args* a, void* str
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
   p.wi_chunk = wi_chunk(a->max_seqlen, a->head_dim, 1, p.group);
+  fa::set_work_map(p);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = (float)((double)a->scale * a->q_descale * a->k_descale * 1.4426950408889634073599);
   p.o_scale = a->v_descale;
@@ -432,6 +436,7 @@ fa_status paged_impl(const fa_fwd_paged_args* a, const float* fp8, const char* f
   p.group = a->heads_q / a->heads_kv;
   p.num_qtiles = (int32_t)qtiles;
   p.wi_chunk = wi_chunk(a->max_seqlen_k, a->head_dim, fp8 ? 1 : 2, p.group);
+  fa::set_work_map(p);
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = fp8 ? (float)((double)a->scale * fp8[0] * fp8[1] * 1.4426950408889634073599) : scale_log2(a->scale);
   p.o_scale = fp8 ? fp8[2] : 1.f;

@@ -159,45 +159,6 @@ __device__ __forceinline__ uint32_t keep_mask16(uint32_t w, uint32_t tm1) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, d) >> (short)15);
 }
 
-// Work item of prefill workgroup w of nwg = num_qtiles x (sequence, query
-// head) pairs: query tile qt and pair bh = b * heads_q + h.  Workgroups are
-// dealt round-robin to the 8 XCDs and each XCD starts its items in order as
-// its CUs free up.  When the GQA groups (the `group` query heads that share a
-// KV head) split evenly over the XCDs, group g goes to XCD g mod 8: every XCD
-// then holds a share of every sequence, so the causal work of packed
-// sequences of different lengths balances across XCDs, and the heads of a
-// group share its K/V in one XCD's L2.  Each XCD starts with the heaviest
-// causal items (the last query tiles of all its pairs), then the ones
-// before, and so on.  With chunk > 0 the XCD's pairs are taken `chunk` at a
-// time (a multiple of the group) and each chunk's items run heaviest first
-// before the next chunk starts: the XCD's CUs then work on few pairs at once
-// and their query tiles share each K/V tile through the L2, where a
-// heaviest-first order over many long packed sequences would keep more K/V
-// in flight than the L2 holds.
-__host__ __device__ inline void prefill_work_item(int nwg, int w, int num_qtiles, int group, int chunk, int& qt,
-                                           int& bh) {
-  const int npairs = nwg / num_qtiles;
-  if ((npairs / group) % 8 == 0 && npairs % group == 0) {
-    const int px = npairs / 8;  // pairs per XCD
-    const int j = w / 8;        // rank of this workgroup on its XCD
-    int k;                      // the XCD's k-th pair
-    if (chunk > 0) {
-      const int c0 = j / (chunk * num_qtiles) * chunk;  // the chunk's first pair
-      const int cn = min(chunk, px - c0);               // pairs in this chunk
-      const int r = j - c0 * num_qtiles;
-      k = c0 + r % cn;
-      qt = num_qtiles - 1 - r / cn;
-    } else {
-      k = j % px;
-      qt = num_qtiles - 1 - j / px;
-    }
-    bh = ((k / group) * 8 + w % 8) * group + k % group;
-  } else {
-    qt = num_qtiles - 1 - (w % num_qtiles);
-    bh = w / num_qtiles;
-  }
-}
-
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

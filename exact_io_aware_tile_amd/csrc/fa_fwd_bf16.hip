@@ -123,9 +123,9 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
 
   // Work item: XCD-balanced, longest first (prefill_work_item).
   int qt, bh;
-  prefill_work_item(gridDim.x, blockIdx.x, p.num_qtiles, p.group, p.wi_chunk, qt, bh);
-  const int h = bh % p.heads_q;
-  const int b = bh / p.heads_q;
+  prefill_work_item(p.wmap, blockIdx.x, qt, bh);
+  const int b = idiv(bh, p.by_heads);
+  const int h = bh - b * p.heads_q;
 
   int nq, nk;
   int64_t q_base, k_base, v_base, o_base, lse_base;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(const FwdParams p) {
   }
   const int q0 = qt * kBr;
   if (q0 >= nq) return;  // uniform over the workgroup
-  const int g = h / p.group;
+  const int g = idiv(h, p.wmap.by_group);
   q_base += (int64_t)h * p.q_hs;
   k_base += (int64_t)g * (PAGED ? p.p_hs : p.k_hs);
   v_base += (int64_t)g * (PAGED ? p.p_hs : p.v_hs);

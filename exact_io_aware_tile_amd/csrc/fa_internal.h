@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_workmap.h"
+
 namespace fa {
 
 // Query rows handled by one prefill workgroup.
@@ -63,7 +65,18 @@ struct FwdParams {
   // Work mapping: 0 = every XCD runs its pairs' heaviest items first; > 0 =
   // pairs taken that many at a time (packed sequences, see prefill_work_item).
   int32_t wi_chunk;
+  WorkMap wmap;     // the mapping of this launch (set_work_map)
+  IntDiv by_heads;  // pair -> (sequence, head)
 };
+
+// The work mapping of a prefill launch over num_qtiles * heads_q * batch
+// workgroups, with its divisors prepared here rather than in every
+// workgroup.
+inline void set_work_map(FwdParams& p) {
+  const int64_t nwg = (int64_t)p.num_qtiles * p.heads_q * p.batch;
+  p.wmap = nwg > 0 ? make_workmap((int32_t)nwg, p.num_qtiles, p.group, p.wi_chunk) : make_workmap(1, 1, 1, 0);
+  p.by_heads = make_intdiv(p.heads_q > 0 ? p.heads_q : 1);
+}
 
 // Paged decode: query heads per kv head (one wave serves the whole group),
 // and the largest pool token stride (elements) the kernel's 32-bit per-lane

@@ -1,11 +1,14 @@
 """The prefill work mapping is a bijection (CPU only).
 
 Builds ``tests/work_mapping_check.cpp`` with hipcc for the host (it includes
-the kernels' own ``fa_device.h``, so the code checked is the code the kernels
+the kernels' own ``fa_workmap.h``, so the code checked is the code the kernels
 run) and runs it: over query-tile counts, pair counts, GQA group sizes and
 chunk sizes (0 = the plain heaviest-first order, and sizes that do and do not
 divide the XCD's pairs) every workgroup index maps to a distinct in-range
-(query tile, pair).
+(query tile, pair), in the same order as the mapping written with plain
+integer divisions; and the multiply-and-shift division the mapping uses
+equals integer division exhaustively for small operands and on edge and
+random operands up to 2^31 - 1.
 """
 import os
 import shutil
