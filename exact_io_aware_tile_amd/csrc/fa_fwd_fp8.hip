@@ -68,7 +68,10 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Four weights -> four E4M3 bytes (nearest-even), a first.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // The first conversion writes the low half of a's register in place (its
+  // upper half, a's old bits, is overwritten by the second), so no register
+  // is cleared for it.
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
@@ -170,8 +173,9 @@ __global__ __launch_bounds__(kThreads) void fwd_fp8_kernel(const FwdParams p) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
   f32x16 lsum = zero16();   // every register: the sum of this row's rounded weights
-  const i32x8 ones = {(int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3,
-                      (int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3};
+  i32x8 ones = {(int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3,
+                (int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3, (int)kOnesE4M3};
+  asm volatile("" : "+v"(ones));  // opaque: kept in registers, not rebuilt every tile
   float m_run = -INFINITY;  // base-2 reference max of this lane's row
   float l_run = 0.f;        // this half-wave's share of the fp32 sum of weights
   const float c = p.scale_log2;
