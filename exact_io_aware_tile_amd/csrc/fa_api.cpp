@@ -592,6 +592,8 @@ FA_EXPORT fa_status fa_merge_states(const fa_merge_states_args* a, void* stream)
   if (rows == 0) return ok();
   if ((double)a->num_parts * (double)rows * a->head_dim >= 1099511627776.0)
     return fail(FA_ERR_UNSUPPORTED, "fa_merge_states: more than 2^40 input elements");
+  if (rows * a->head_dim >= (int64_t(1) << 34))
+    return fail(FA_ERR_UNSUPPORTED, "fa_merge_states: 2^34 or more elements per part");
   if (!a->o_parts || !a->lse_parts || !a->o) return fail(FA_ERR_NULL_POINTER, "fa_merge_states: NULL tensor");
   if (!aligned16(a->o_parts) || !aligned16(a->lse_parts) || !aligned16(a->o) || (a->lse && !aligned16(a->lse)))
     return fail(FA_ERR_BAD_SHAPE, "fa_merge_states: pointers must be 16-byte aligned");
@@ -608,6 +610,8 @@ FA_EXPORT fa_status fa_merge_states(const fa_merge_states_args* a, void* stream)
   p.heads = a->heads;
   p.head_dim = a->head_dim;
   p.f32 = a->dtype == FA_F32;
+  p.by_heads = fa::make_intdiv(a->heads > 0 ? a->heads : 1);
+  p.by_seqlen = fa::make_intdiv(a->seqlen > 0 ? a->seqlen : 1);
   const hipError_t e = fa::launch_merge(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_merge_states: %s", hipGetErrorString(e));
   return ok();

@@ -135,6 +135,7 @@ struct MergeParams {
   int64_t part_rows;      // rows
   int32_t parts, seqlen, heads, head_dim;
   int32_t f32;
+  IntDiv by_heads, by_seqlen;  // row -> (batch, seqlen, head) (rows * head_dim / 8 < 2^31)
 };
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 

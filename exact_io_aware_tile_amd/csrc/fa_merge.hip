@@ -51,18 +51,21 @@ __device__ __forceinline__ void load8(const void* base, int64_t e, float (&x)[8]
 template <int D, bool F32>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
   constexpr int CPR = D / 8;  // lanes per row
-  const int64_t n = p.rows * CPR;
+  const int64_t n = p.rows * CPR;  // < 2^31
   const float kLog2e = 1.4426950408889634f;
+  // Lane indices stay below 2^31 (the host bounds a part below 2^34
+  // elements), so a row splits into (batch, seqlen, head) by the divisors
+  // the host prepared, without any runtime division.
   for (int64_t i = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kMergeThreads) {
-    const int64_t r = i / CPR;  // row (b, s, h) of the [batch, seqlen, heads] order
-    const int c = (int)(i % CPR);
-    const int64_t bs = r / p.heads;
-    const int h = (int)(r % p.heads);
-    const int64_t b = bs / p.seqlen;
-    const int64_t s = bs % p.seqlen;
-    const int64_t li = (b * p.heads + h) * p.seqlen + s;  // [batch, heads, seqlen] order
-    const int64_t e = r * D + 8 * c;
+    const int r = (int)i / CPR;  // row (b, s, h) of the [batch, seqlen, heads] order
+    const int c = (int)i % CPR;
+    const int bs = idiv(r, p.by_heads);
+    const int h = r - bs * p.heads;
+    const int b = idiv(bs, p.by_seqlen);
+    const int s = bs - b * p.seqlen;
+    const int64_t li = ((int64_t)b * p.heads + h) * p.seqlen + s;  // [batch, heads, seqlen] order
+    const int64_t e = (int64_t)r * D + 8 * c;
 
     // One pass over the parts in groups of kGroup: a group's loads (its
     // log-sum-exps and output rows) are all issued before any is used, the

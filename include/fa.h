@@ -447,7 +447,9 @@ int32_t fa_decode_paged_fp8_num_splits(const fa_decode_paged_fp8_args *args);
  * A row with lse_p = -inf in every part gets o = 0 and lse = -inf.  The
  * dense (seqlen = N), packed (batch = 1, seqlen = total tokens) and decode
  * (seqlen = 1) outputs all have this layout.  All pointers 16-byte
- * aligned; P * batch * seqlen * heads * head_dim below 2^40.
+ * aligned; P * batch * seqlen * heads * head_dim below 2^40 and
+ * batch * seqlen * heads * head_dim below 2^34 (FA_ERR_UNSUPPORTED
+ * otherwise).
  */
 typedef struct {
   int32_t num_parts, batch, seqlen, heads, head_dim;

@@ -524,6 +524,7 @@ def merge_args(**kw):
     (dict(o=0x3008), fa.FA_ERR_BAD_SHAPE),
     (dict(lse=0x4004), fa.FA_ERR_BAD_SHAPE),
     (dict(num_parts=1 << 20, batch=1 << 10, seqlen=1 << 10), fa.FA_ERR_UNSUPPORTED),
+    (dict(num_parts=1, batch=1 << 10, seqlen=1 << 13, heads=1 << 4), fa.FA_ERR_UNSUPPORTED),  # 2^34 per part
 ])
 def test_merge_rejects_before_launch(L, kw, status):
     a = merge_args(**kw)
