@@ -10,7 +10,7 @@ The race-check library (``_build/libfa_gfx950_synccheck.so``, built by
 ``build()`` from the same sources with FA_SYNC_CHECK) drains every memory
 operation at each such wait and uses a full ``__syncthreads`` at each
 barrier, so it cannot read a stage early.  Each case here runs the product
-and the checker on the same inputs and requires identical bits in O and LSE:
+and the checking build on the same inputs and requires identical bits in O and LSE:
 the arithmetic is the same instruction stream, so any difference is a
 synchronisation error of the product.  Cases cover 1, 2 and 3 key tiles
 (the pipeline's prologue and drain), many tiles with a ragged tail, several
@@ -53,7 +53,7 @@ def using(fa, L):
 
 
 def both(libs, fn):
-    """Run fn(fa) with the product and with the checker; compare every
+    """Run fn(fa) with the product and with the checking build; compare every
     output tensor bit for bit."""
     fa, prod, chk = libs
     with using(fa, prod):
